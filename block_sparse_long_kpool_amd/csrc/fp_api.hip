@@ -1,0 +1,267 @@
+// C ABI of the library: argument validation, size queries, workspace layout
+// and kernel launches.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "fp_internal.hpp"
+
+using namespace fp;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Validate the descriptor and fill the launch geometry.
+int make_geometry(const fp_problem* p, Geometry* g) {
+  if (!p) return fail(FP_ERR_INVALID, "problem descriptor is NULL");
+  if (p->num_seqs < 1) return fail(FP_ERR_INVALID, "num_seqs must be >= 1 (got %d)", p->num_seqs);
+  if (!p->cu_seqlens_host || !p->cu_seqlens_dev)
+    return fail(FP_ERR_INVALID, "cu_seqlens_host and cu_seqlens_dev must be non-NULL");
+  if (p->head_dim != kHeadDim) return fail(FP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", p->head_dim);
+  if (p->block_size != kBlock) return fail(FP_ERR_UNSUPPORTED, "block_size must be 128 (got %d)", p->block_size);
+  if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads)
+    return fail(FP_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads / p->num_kv_heads > 16)
+    return fail(FP_ERR_UNSUPPORTED, "GQA group size %d > 16", p->num_q_heads / p->num_kv_heads);
+  const int P = p->page_size;
+  if (P < 1 || !((kBlock % P == 0) || (P % kBlock == 0)))
+    return fail(FP_ERR_UNSUPPORTED, "page_size %d must divide 128 or be a multiple of 128", P);
+  if (!p->page_table_dev) return fail(FP_ERR_INVALID, "page_table_dev is NULL");
+  if (p->num_pages < 1) return fail(FP_ERR_INVALID, "num_pages must be >= 1");
+  const int qk = p->qk_dtype, vd = p->v_dtype, od = p->out_dtype;
+  const bool combo = (qk == FP_BF16 && vd == FP_BF16) || (qk == FP_E4M3 && vd == FP_BF16) ||
+                     (qk == FP_F32 && vd == FP_F32);
+  if (!combo) return fail(FP_ERR_UNSUPPORTED, "dtype combination qk=%d v=%d not supported", qk, vd);
+  if (od != FP_F32 && od != FP_BF16) return fail(FP_ERR_UNSUPPORTED, "out_dtype %d not supported", od);
+  if (qk == FP_E4M3 && (!p->q_scale_dev || !p->k_scale_dev))
+    return fail(FP_ERR_INVALID, "e4m3 inputs need q_scale_dev and k_scale_dev");
+  const int32_t* cu = p->cu_seqlens_host;
+  if (cu[0] != 0) return fail(FP_ERR_INVALID, "cu_seqlens[0] must be 0");
+  int64_t nblk = 0;
+  int maxn = 0, maxlen = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int len = cu[s + 1] - cu[s];
+    if (len < 0) return fail(FP_ERR_INVALID, "cu_seqlens must be nondecreasing (seq %d)", s);
+    const int n = (len + kBlock - 1) / kBlock;
+    nblk += n;
+    maxn = std::max(maxn, n);
+    maxlen = std::max(maxlen, len);
+  }
+  if (nblk < 1) return fail(FP_ERR_INVALID, "batch has no tokens");
+  if (maxn > kMaxBlocksPerSeq)
+    return fail(FP_ERR_UNSUPPORTED, "sequence of %d blocks exceeds the %d-block limit", maxn, kMaxBlocksPerSeq);
+  if ((int64_t)p->max_pages_per_seq * P < maxlen)
+    return fail(FP_ERR_INVALID, "max_pages_per_seq * page_size (%lld) < longest sequence (%d)",
+                (long long)p->max_pages_per_seq * P, maxlen);
+  g->num_seqs = p->num_seqs;
+  g->hq = p->num_q_heads;
+  g->hkv = p->num_kv_heads;
+  g->group = p->num_q_heads / p->num_kv_heads;
+  g->page_size = P;
+  g->max_pages = p->max_pages_per_seq;
+  g->num_blocks = nblk;
+  g->max_blocks = maxn;
+  g->num_rows = nblk * p->num_kv_heads;
+  g->total_tokens = cu[p->num_seqs];
+  g->qk_dtype = qk;
+  g->v_dtype = vd;
+  g->out_dtype = od;
+  g->softmax_scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  return FP_OK;
+}
+
+struct DiscoverWs { int32_t* boff; u16* km16; };
+struct SelectWs { int32_t* boff; uint32_t* bits; int32_t* counts; };
+struct AttnWs { int32_t* boff; u16* km16; u16* vm16; };
+
+size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
+  char* b = reinterpret_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* ptr = b ? b + off : nullptr;
+    off = align_up(off + bytes);
+    return ptr;
+  };
+  const size_t boff_bytes = sizeof(int32_t) * (size_t)(g.num_seqs + 1);
+  const size_t pooled16 = sizeof(u16) * (size_t)g.hkv * (size_t)g.num_blocks * kHeadDim;
+  if (which == FP_WS_DISCOVER) {
+    DiscoverWs w;
+    w.boff = (int32_t*)take(boff_bytes);
+    w.km16 = (u16*)take(2 * pooled16);  // hi part, then lo part
+    if (out) *reinterpret_cast<DiscoverWs*>(out) = w;
+  } else if (which == FP_WS_SELECT) {
+    SelectWs w;
+    const size_t words = (size_t)(g.max_blocks + 31) / 32;
+    w.boff = (int32_t*)take(boff_bytes);
+    w.bits = (uint32_t*)take(sizeof(uint32_t) * words * (size_t)g.num_rows);
+    w.counts = (int32_t*)take(sizeof(int32_t) * (size_t)g.num_rows);
+    if (out) *reinterpret_cast<SelectWs*>(out) = w;
+  } else if (which == FP_WS_ATTN) {
+    AttnWs w;
+    w.boff = (int32_t*)take(boff_bytes);
+    w.km16 = (u16*)take(pooled16);
+    w.vm16 = (u16*)take(pooled16);
+    if (out) *reinterpret_cast<AttnWs*>(out) = w;
+  } else {
+    return 0;
+  }
+  return off;
+}
+
+int check_ws(const Geometry& g, int which, void* ws, size_t ws_bytes) {
+  const size_t need = ws_layout(g, which, nullptr, nullptr);
+  if (!ws) return fail(FP_ERR_INVALID, "workspace pointer is NULL");
+  if (ws_bytes < need)
+    return fail(FP_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(FP_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  return FP_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FP_OK;
+  return fail(FP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fp_num_blocks(const fp_problem* p) {
+  Geometry g;
+  return make_geometry(p, &g) == FP_OK ? g.num_blocks : -1;
+}
+
+int32_t fp_max_blocks(const fp_problem* p) {
+  Geometry g;
+  return make_geometry(p, &g) == FP_OK ? g.max_blocks : -1;
+}
+
+int64_t fp_num_rows(const fp_problem* p) {
+  Geometry g;
+  return make_geometry(p, &g) == FP_OK ? g.num_rows : -1;
+}
+
+int64_t fp_scores_elems(const fp_problem* p) {
+  Geometry g;
+  return make_geometry(p, &g) == FP_OK ? g.num_rows * (int64_t)g.max_blocks : -1;
+}
+
+int64_t fp_csr_capacity(const fp_problem* p) {
+  Geometry g;
+  if (make_geometry(p, &g) != FP_OK) return -1;
+  int64_t c = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t n = (p->cu_seqlens_host[s + 1] - p->cu_seqlens_host[s] + kBlock - 1) / kBlock;
+    c += n * (n + 1) / 2;
+  }
+  return c * g.hkv;
+}
+
+size_t fp_workspace_bytes(const fp_problem* p, int32_t which) {
+  Geometry g;
+  if (make_geometry(p, &g) != FP_OK) return 0;
+  return ws_layout(g, which, nullptr, nullptr);
+}
+
+const char* fp_status_string(int32_t status) {
+  switch (status) {
+    case FP_OK: return "ok";
+    case FP_ERR_INVALID: return "invalid argument";
+    case FP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FP_ERR_WORKSPACE: return "workspace too small";
+    case FP_ERR_CAPACITY: return "col_idx capacity too small";
+    case FP_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* fp_last_error(void) { return g_err; }
+
+int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                float* k_mean, float* v_mean, float* block_scores, void* ws, size_t ws_bytes,
+                void* stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !k_mean || !v_mean || !block_scores)
+    return fail(FP_ERR_INVALID, "fp_discover: a tensor pointer is NULL");
+  if ((st = check_ws(g, FP_WS_DISCOVER, ws, ws_bytes))) return st;
+  DiscoverWs w;
+  ws_layout(g, FP_WS_DISCOVER, ws, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = hip_status(launch_plan(p->cu_seqlens_dev, g.num_seqs, w.boff, s), "plan"))) return st;
+  if ((st = hip_status(launch_pool(g, p->cu_seqlens_dev, w.boff, p->page_table_dev, k_cache, v_cache,
+                                   p->k_scale_dev, k_mean, v_mean, w.km16, s), "pool")))
+    return st;
+  return hip_status(launch_scores(g, p->cu_seqlens_dev, w.boff, q, p->q_scale_dev, w.km16,
+                                  block_scores, s), "scores");
+}
+
+int fp_select(const fp_problem* p, const void* q, const float* k_mean, const float* block_scores,
+              float alpha, int32_t sink_tokens, int32_t local_tokens, int32_t* row_ptr,
+              int32_t* col_idx, int64_t col_capacity, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st) return st;
+  if (!q || !k_mean || !block_scores || !row_ptr || !col_idx)
+    return fail(FP_ERR_INVALID, "fp_select: a tensor pointer is NULL");
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(FP_ERR_INVALID, "sink_tokens and local_tokens must be >= 0");
+  if (isnan(alpha)) return fail(FP_ERR_INVALID, "alpha is NaN");
+  const int64_t cap = fp_csr_capacity(p);
+  if (col_capacity < cap)
+    return fail(FP_ERR_CAPACITY, "col_capacity %lld < %lld (every causal block kept)",
+                (long long)col_capacity, (long long)cap);
+  if ((st = check_ws(g, FP_WS_SELECT, ws, ws_bytes))) return st;
+  SelectWs w;
+  ws_layout(g, FP_WS_SELECT, ws, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int n_sink = (sink_tokens + kBlock - 1) / kBlock;
+  const int n_local = std::max(1, (local_tokens + kBlock - 1) / kBlock);
+  if ((st = hip_status(launch_plan(p->cu_seqlens_dev, g.num_seqs, w.boff, s), "plan"))) return st;
+  return hip_status(launch_select(g, p->cu_seqlens_dev, w.boff, q, p->q_scale_dev, k_mean, block_scores,
+                                  alpha, n_sink, n_local, w.bits, w.counts, row_ptr, col_idx, s),
+                    "select");
+}
+
+int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* row_ptr, const int32_t* col_idx, const float* k_mean,
+                         const float* v_mean, int32_t mean_correction, void* out, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !row_ptr || !col_idx || !out)
+    return fail(FP_ERR_INVALID, "fp_sparse_attn_paged: a tensor pointer is NULL");
+  if (mean_correction && (!k_mean || !v_mean))
+    return fail(FP_ERR_INVALID, "mean correction needs k_mean and v_mean");
+  if ((st = check_ws(g, FP_WS_ATTN, ws, ws_bytes))) return st;
+  AttnWs w;
+  ws_layout(g, FP_WS_ATTN, ws, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = hip_status(launch_attn_prep(g, p->cu_seqlens_dev, w.boff, mean_correction ? k_mean : nullptr,
+                                        v_mean, w.km16, w.vm16, s), "attn prep")))
+    return st;
+  return hip_status(launch_attn(g, p->cu_seqlens_dev, w.boff, p->page_table_dev, q, k_cache, v_cache,
+                                p->q_scale_dev, p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
+                                mean_correction ? 1 : 0, out, lse, s),
+                    "attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Block pooling: mean of K and V over each 128-token block of the paged
+// cache (FlashPrefill summary "长上下文加速 28 倍", 3.1 key pooling; FlashPrefill
+// V2 paper reading 4.1, the block means kbar_J / vbar_J).  HBM-bound: every
+// K/V element is read exactly once.
+#include "fp_internal.hpp"
+
+namespace fp {
+
+// One workgroup: boff[s] = sum_{s' < s} ceil(len_s' / 128), chunked scan.
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int num_seqs,
+                                                   int32_t* __restrict__ boff) {
+  __shared__ int buf[256];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < num_seqs; base += 256) {
+    int s = base + (int)threadIdx.x;
+    int n = 0;
+    if (s < num_seqs) n = (cu[s + 1] - cu[s] + kBlock - 1) / kBlock;
+    buf[threadIdx.x] = n;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      int v = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int incl = buf[threadIdx.x];
+    int c = carry;
+    if (s < num_seqs) boff[s] = c + incl - n;
+    __syncthreads();
+    if (threadIdx.x == 255) carry = c + incl;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) boff[num_seqs] = carry;
+}
+
+hipError_t launch_plan(const int32_t* cu, int num_seqs, int32_t* boff, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, cu, num_seqs, boff);
+  return hipGetLastError();
+}
+
+// Load 8 consecutive elements of one token row as float.  fp32 inputs are
+// rounded to bf16 first: that is the value every kernel of the library uses.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) {
+  if constexpr (DT == FP_BF16) {
+    const uint4 r = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(base) + elem);
+    const unsigned w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else if constexpr (DT == FP_E4M3) {
+    const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + elem);
+    const unsigned w[2] = {r.x, r.y};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e4m3_to_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    const float4 a = p[0], b = p[1];
+    const float t[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)f32_to_bf16(t[i]);
+  }
+}
+
+// grid (N blocks, Hkv, 2 = {K, V}); 256 threads = 16 token lanes x 16 chunks
+// of 8 head-dim elements.  Summation order is fixed (deterministic).
+template <int KDT, int VDT>
+__global__ __launch_bounds__(256) void pool_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ boff, int num_seqs,
+    const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
+    int64_t num_blocks, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const float* __restrict__ k_scale, float* __restrict__ k_mean, float* __restrict__ v_mean,
+    u16* __restrict__ k_mean_bf16) {
+  __shared__ float red[16][kHeadDim + 4];
+  const int gb = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z == 1;
+  const int s = find_seq(boff, num_seqs, gb);
+  const int J = gb - boff[s];
+  const int len = cu[s + 1] - cu[s];
+  const int p0 = J * kBlock;
+  const int nJ = min(kBlock, len - p0);
+  const int chunk = threadIdx.x & 15;
+  const int tl = threadIdx.x >> 4;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int t = tl; t < nJ; t += 16) {
+    const int p = p0 + t;
+    const int page = page_table[(int64_t)s * max_pages + p / page_size];
+    const int64_t elem = (((int64_t)page * page_size + p % page_size) * hkv + h) * kHeadDim + chunk * 8;
+    float v[8];
+    if (is_v) load8<VDT>(v_cache, elem, v); else load8<KDT>(k_cache, elem, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[tl][chunk * 8 + i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    const int d = threadIdx.x;
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += red[r][d];
+    float mean = sum / (float)nJ;
+    if (!is_v && KDT == FP_E4M3) mean *= k_scale[h];
+    const int64_t o = ((int64_t)h * num_blocks + gb) * kHeadDim + d;
+    if (is_v) {
+      v_mean[o] = mean;
+    } else {
+      // two-term bf16 split (hi + lo) of the fp32 mean for the discovery MFMA
+      k_mean[o] = mean;
+      const __bf16 hi = f32_to_bf16(mean);
+      const __bf16 lo = f32_to_bf16(mean - (float)hi);
+      const int64_t nel = (int64_t)hkv * num_blocks * kHeadDim;
+      k_mean_bf16[o] = __builtin_bit_cast(u16, hi);
+      k_mean_bf16[nel + o] = __builtin_bit_cast(u16, lo);
+    }
+  }
+}
+
+hipError_t launch_pool(const Geometry& g, const int32_t* cu, const int32_t* boff,
+                       const int32_t* page_table, const void* k_cache, const void* v_cache,
+                       const float* k_scale, float* k_mean, float* v_mean, u16* k_mean_bf16,
+                       hipStream_t st) {
+  dim3 grid((unsigned)g.num_blocks, (unsigned)g.hkv, 2);
+#define FP_POOL(KD, VD)                                                                       \
+  hipLaunchKernelGGL((pool_kernel<KD, VD>), grid, dim3(256), 0, st, cu, boff, g.num_seqs,     \
+                     page_table, g.max_pages, g.page_size, g.hkv, g.num_blocks, k_cache,      \
+                     v_cache, k_scale, k_mean, v_mean, k_mean_bf16)
+  if (g.qk_dtype == FP_BF16 && g.v_dtype == FP_BF16) FP_POOL(FP_BF16, FP_BF16);
+  else if (g.qk_dtype == FP_E4M3 && g.v_dtype == FP_BF16) FP_POOL(FP_E4M3, FP_BF16);
+  else if (g.qk_dtype == FP_F32 && g.v_dtype == FP_F32) FP_POOL(FP_F32, FP_F32);
+  else return hipErrorInvalidValue;
+#undef FP_POOL
+  return hipGetLastError();
+}
+
+}  // namespace fp

@@ -1,0 +1,256 @@
+// Max-based dynamic threshold, forced sink/local blocks and index compaction
+// (FlashPrefill summary "长上下文加速 28 倍", 3.2: keep J when its score reaches
+// alpha times the row maximum over J <= I, plus the first 256 and the last
+// 512 tokens as a safety net; 3.3: compact the kept blocks into a dense list
+// so the attention loop walks only them).
+//
+// Three kernels:
+//   decide  one wave per CSR row: re-weight (subtract the row max of the log
+//           scores), threshold, forced blocks -> keep bitmask + count.
+//           Entries whose fast (bf16) score lies within kGuard of the
+//           threshold are re-evaluated in float64 from q and k_mean, with
+//           the row maximum re-evaluated the same way, so that every
+//           decision matches exact arithmetic.
+//   scan    one workgroup: exclusive prefix sum of the counts -> row_ptr.
+//   compact one wave per row: wavefront ballot + popcount prefix writes the
+//           kept block indices in ascending order.
+#include "fp_internal.hpp"
+
+namespace fp {
+
+namespace {
+
+// Fast-path error budget (natural-log units).  The discovery logits use the
+// pooled keys split into two bf16 terms (hi + lo, relative residual ~2^-17)
+// with fp32 MFMA accumulation; on attention-scale logits (|x| ~ 25) that
+// leaves absolute errors of a few 1e-5.  Every entry whose fast score lies
+// within kGuard of the threshold (and every candidate within kGuard of the
+// row max) is re-evaluated in float64, so decisions outside that window have
+// a margin of ~50x the fast path's error.
+constexpr float kGuard = 2e-3f;
+constexpr int kRowsPerWg = 4;
+
+template <int QDT>
+__device__ __forceinline__ double q_elem(const void* q, int64_t e) {
+  if constexpr (QDT == FP_BF16) {
+    return (double)bf16_bits_to_f32(reinterpret_cast<const u16*>(q)[e]);
+  } else if constexpr (QDT == FP_E4M3) {
+    return (double)e4m3_to_f32(reinterpret_cast<const uint8_t*>(q)[e]);
+  } else {
+    return (double)(float)f32_to_bf16(reinterpret_cast<const float*>(q)[e]);
+  }
+}
+
+// Exact log2-free score of pooled key J for the rows of (h, block I):
+// ln sum_r exp(x_rJ - ref) + ref, all in float64.  One wave.
+template <int QDT>
+__device__ double exact_score(const void* q, const float* q_scale, const float* kbar, int hq,
+                              int group, int h, int64_t tok0, int nI, double scale, double ref,
+                              int lane) {
+  const int R = group * nI;
+  double acc = 0.0;
+  for (int r = lane; r < R; r += 64) {
+    const int hh = r / nI;
+    const int t = r - hh * nI;
+    const int hq_idx = h * group + hh;
+    const int64_t e0 = ((tok0 + t) * hq + hq_idx) * (int64_t)kHeadDim;
+    double dot = 0.0;
+    for (int d = 0; d < kHeadDim; ++d) dot = fma(q_elem<QDT>(q, e0 + d), (double)kbar[d], dot);
+    double x = scale * dot;
+    if constexpr (QDT == FP_E4M3) x *= (double)q_scale[hq_idx];
+    acc += exp(x - ref);
+  }
+  acc = wave_sum_d(acc);
+  return log(acc) + ref;
+}
+
+template <int QDT>
+__global__ __launch_bounds__(256) void decide_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ boff, int num_seqs, int hq,
+    int hkv, int group, int64_t num_blocks, int max_blocks, float softmax_scale,
+    const void* __restrict__ q, const float* __restrict__ q_scale,
+    const float* __restrict__ k_mean, const float* __restrict__ scores, float alpha, int n_sink,
+    int n_local, uint32_t* __restrict__ keep_bits, int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + (threadIdx.x >> 6);
+  if (row >= (int64_t)hkv * num_blocks) return;
+  const int h = (int)(row / num_blocks);
+  const int gb = (int)(row % num_blocks);
+  const int s = find_seq(boff, num_seqs, gb);
+  const int I = gb - boff[s];
+  const int words = (max_blocks + 31) >> 5;
+  uint32_t* bits = keep_bits + row * words;
+  const float* L = scores + row * max_blocks;
+  const int ncols = I + 1;
+
+  if (!(alpha > 0.f)) {  // alpha <= 0 (or NaN): every causal block
+    for (int w = lane; w < words; w += 64) {
+      const int lo = 32 * w;
+      bits[w] = lo >= ncols ? 0u : (ncols - lo >= 32 ? 0xFFFFFFFFu : ((1u << (ncols - lo)) - 1u));
+    }
+    if (lane == 0) counts[row] = ncols;
+    return;
+  }
+
+  // row max of the fast log scores (re-weighting against the top block)
+  float lmax = -INFINITY;
+  for (int J = lane; J < ncols; J += 64) lmax = fmaxf(lmax, L[J]);
+  lmax = wave_max(lmax);
+  const float lna = __logf(alpha);
+  const float thr = lna + lmax;
+
+  // any entry close enough to the threshold to need exact evaluation?
+  bool need = false;
+  for (int J = lane; J < ncols; J += 64) {
+    const bool forced = J < n_sink || I - J < n_local;
+    need |= (!forced && fabsf(L[J] - thr) <= kGuard);
+  }
+  need = __any(need);
+
+  double ex_thr = 0.0;
+  if (need) {
+    const int len = cu[s + 1] - cu[s];
+    const int nI = min(kBlock, len - I * kBlock);
+    const int64_t tok0 = (int64_t)cu[s] + (int64_t)I * kBlock;
+    const float* kb = k_mean + ((int64_t)h * num_blocks + boff[s]) * kHeadDim;
+    const double ref = (double)lmax;
+    double emax = -INFINITY;
+    // exact maximum over every candidate for the row maximum
+    for (int base = 0; base < ncols; base += 64) {
+      const int J = base + lane;
+      const bool cand = J < ncols && L[J] >= lmax - kGuard;
+      unsigned long long m = __ballot(cand);
+      while (m) {
+        const int b = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const double e = exact_score<QDT>(q, q_scale, kb + (int64_t)(base + b) * kHeadDim, hq,
+                                          group, h, tok0, nI, (double)softmax_scale, ref, lane);
+        emax = fmax(emax, e);
+      }
+    }
+    ex_thr = log((double)alpha) + emax;
+  }
+
+  int count = 0;
+  // every word of the row is written (blocks past the diagonal are zero)
+  for (int base = 0; base < 32 * words; base += 64) {
+    const int J = base + lane;
+    bool keep = false, recheck = false;
+    if (J < ncols) {
+      const bool forced = J < n_sink || I - J < n_local;
+      keep = forced || L[J] >= thr;
+      recheck = need && !forced && fabsf(L[J] - thr) <= kGuard;
+    }
+    unsigned long long m = __ballot(recheck);
+    if (m) {
+      const int len = cu[s + 1] - cu[s];
+      const int nI = min(kBlock, len - I * kBlock);
+      const int64_t tok0 = (int64_t)cu[s] + (int64_t)I * kBlock;
+      const float* kb = k_mean + ((int64_t)h * num_blocks + boff[s]) * kHeadDim;
+      while (m) {
+        const int b = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const double e = exact_score<QDT>(q, q_scale, kb + (int64_t)(base + b) * kHeadDim, hq,
+                                          group, h, tok0, nI, (double)softmax_scale,
+                                          (double)lmax, lane);
+        if (lane == b) keep = e >= ex_thr;
+      }
+    }
+    const unsigned long long kb64 = __ballot(keep);
+    count += __popcll(kb64);
+    if (lane == 0) {
+      const int w = base >> 5;
+      bits[w] = (uint32_t)kb64;
+      if (w + 1 < words) bits[w + 1] = (uint32_t)(kb64 >> 32);
+    }
+  }
+  if (lane == 0) counts[row] = count;
+}
+
+// Exclusive scan of counts[nrows] -> row_ptr[nrows + 1] (one workgroup).
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
+                                                    int64_t nrows, int32_t* __restrict__ row_ptr) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < nrows; base += 1024) {
+    const int64_t i = base + tid;
+    const int32_t v = i < nrows ? counts[i] : 0;
+    int32_t x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int32_t w = lane < 16 ? wsum[lane] : 0;
+      for (int o = 1; o < 16; o <<= 1) {
+        const int32_t y = __shfl_up(w, o, 64);
+        if (lane >= o) w += y;
+      }
+      if (lane < 16) wsum[lane] = w;
+    }
+    __syncthreads();
+    const int32_t carry = carry_s;
+    const int32_t excl = carry + (wave ? wsum[wave - 1] : 0) + x - v;
+    if (i < nrows) row_ptr[i] = excl;
+    __syncthreads();
+    if (tid == 1023) carry_s = excl + v;
+    __syncthreads();
+  }
+  if (tid == 0) row_ptr[nrows] = carry_s;
+}
+
+__global__ __launch_bounds__(256) void compact_kernel(int64_t nrows, int max_blocks,
+                                                      const uint32_t* __restrict__ keep_bits,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      int32_t* __restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int words = (max_blocks + 31) >> 5;
+  const uint32_t* bits = keep_bits + row * words;
+  int32_t* dst = col_idx + row_ptr[row];
+  int base_out = 0;
+  for (int base = 0; base < 32 * words; base += 64) {
+    const int w = base >> 5;
+    const uint32_t lo = bits[w];
+    const uint32_t hi = (w + 1 < words) ? bits[w + 1] : 0u;
+    const unsigned long long m = ((unsigned long long)hi << 32) | lo;
+    const bool keep = (m >> lane) & 1ull;
+    const int pos = __popcll(m & ((1ull << lane) - 1ull));
+    if (keep) dst[base_out + pos] = base + lane;
+    base_out += __popcll(m);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const Geometry& g, const int32_t* cu, const int32_t* boff, const void* q,
+                         const float* q_scale, const float* k_mean, const float* scores,
+                         float alpha, int n_sink, int n_local, uint32_t* keep_bits,
+                         int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
+  const unsigned nwg = (unsigned)((g.num_rows + kRowsPerWg - 1) / kRowsPerWg);
+#define FP_DEC(QD)                                                                              \
+  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(256), 0, st, cu, boff, g.num_seqs,     \
+                     g.hq, g.hkv, g.group, g.num_blocks, g.max_blocks, g.softmax_scale, q,        \
+                     q_scale, k_mean, scores, alpha, n_sink, n_local, keep_bits, counts)
+  if (g.qk_dtype == FP_BF16) FP_DEC(FP_BF16);
+  else if (g.qk_dtype == FP_E4M3) FP_DEC(FP_E4M3);
+  else if (g.qk_dtype == FP_F32) FP_DEC(FP_F32);
+  else return hipErrorInvalidValue;
+#undef FP_DEC
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, g.num_rows, row_ptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3(nwg), dim3(256), 0, st, g.num_rows, g.max_blocks,
+                     keep_bits, row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+}  // namespace fp

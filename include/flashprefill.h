@@ -1,0 +1,208 @@
+/*
+ * flashprefill.h -- C ABI of the MI355X (gfx950) block-sparse causal prefill
+ * attention library (FlashPrefill method).
+ *
+ * The method runs in two stages (FlashPrefill V2 paper reading, section 四):
+ * an indexing stage that pools K/V per 128-token block, scores every query
+ * block against the pooled keys and keeps the blocks whose score reaches
+ * alpha times the row maximum plus forced sink and local blocks, emitting
+ * compact per-row index lists; and an attention stage that walks only the
+ * listed blocks of a paged KV cache and folds a block-mean correction for
+ * every pruned block into the same softmax.
+ *
+ * Three calls implement the path, in order:
+ *   fp_discover          pooling + pooled block scores    (indexing, part 1)
+ *   fp_select            threshold + compaction to CSR     (indexing, part 2)
+ *   fp_sparse_attn_paged sparse paged attention + correction (attention)
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer, except fp_problem itself and
+ *     fp_problem.cu_seqlens_host, which live in host memory.
+ *   - The caller owns and allocates every buffer, including the workspace
+ *     (size from fp_workspace_bytes).  The library allocates nothing.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  They never synchronise the host.
+ *   - Return value: FP_OK (0) on success, a negative fp_status otherwise.  On
+ *     error nothing is launched and fp_last_error() returns a message
+ *     (thread-local).  Faults inside kernels (e.g. an out-of-range page id)
+ *     surface at the caller's next synchronisation.
+ *   - Results are deterministic: identical inputs give bit-identical outputs.
+ *   - Shapes: head_dim = 128 and block_size = 128.  T = cu_seqlens[num_seqs]
+ *     tokens, n_s = ceil(len_s / 128) blocks in sequence s, N = sum_s n_s,
+ *     n_max = max_s n_s.
+ *   - Layouts (row-major, innermost last):
+ *       q          [T, Hq, 128]                      dtype qk_dtype
+ *       k_cache    [num_pages, page_size, Hkv, 128]  dtype qk_dtype
+ *       v_cache    [num_pages, page_size, Hkv, 128]  dtype v_dtype
+ *       page_table [num_seqs, max_pages_per_seq] int32: token p of sequence
+ *                  s lives at page page_table[s][p / page_size], slot
+ *                  p % page_size (FlashPrefill V2 article, paged KV section:
+ *                  page base from the table plus in-page offset).
+ *       k_mean, v_mean [Hkv, N, 128] float32 (block b of sequence s at row
+ *                  boff_s + b, boff_s = sum of n over earlier sequences)
+ *       block_scores   [Hkv, N, n_max] float32
+ *       row_ptr    [Hkv * N + 1] int32, rows ordered (kv head, sequence,
+ *                  query block); col_idx int32 block indices inside the
+ *                  sequence, ascending per row.
+ *       out        [T, Hq, 128] dtype out_dtype
+ *       lse        [Hq, T] float32 (natural log), optional
+ *   - Query head hq reads KV head hq / (Hq / Hkv).
+ *   - fp32 Q/K/V are rounded to bf16 (nearest even) when the kernels load
+ *     them; e4m3 values are the OCP E4M3FN codes times a per-head fp32 scale.
+ */
+#ifndef FLASHPREFILL_H
+#define FLASHPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP_F32 = 0,
+  FP_BF16 = 1,
+  FP_E4M3 = 2
+} fp_dtype;
+
+typedef enum {
+  FP_OK = 0,
+  FP_ERR_INVALID = -1,      /* a NULL pointer, a bad size or an inconsistent shape */
+  FP_ERR_UNSUPPORTED = -2,  /* head_dim / block_size / dtype combination not built */
+  FP_ERR_WORKSPACE = -3,    /* ws_bytes smaller than fp_workspace_bytes(...)        */
+  FP_ERR_CAPACITY = -4,     /* col_capacity smaller than fp_csr_capacity(...)       */
+  FP_ERR_HIP = -5           /* a HIP launch error                                   */
+} fp_status;
+
+typedef enum {
+  FP_WS_DISCOVER = 0,
+  FP_WS_SELECT = 1,
+  FP_WS_ATTN = 2
+} fp_workspace_kind;
+
+typedef struct {
+  int32_t num_seqs;                /* >= 1                                            */
+  const int32_t* cu_seqlens_host;  /* HOST   [num_seqs + 1], cu[0] = 0, nondecreasing */
+  const int32_t* cu_seqlens_dev;   /* DEVICE [num_seqs + 1], same values              */
+  int32_t num_q_heads;             /* Hq, a multiple of Hkv, Hq / Hkv <= 16            */
+  int32_t num_kv_heads;            /* Hkv >= 1                                        */
+  int32_t head_dim;                /* must be 128                                     */
+  int32_t block_size;              /* must be 128                                     */
+  int32_t page_size;               /* divides 128, or is a multiple of 128            */
+  int32_t max_pages_per_seq;       /* >= ceil(max_s len_s / page_size)                */
+  int64_t num_pages;               /* pages in k_cache / v_cache; every page id in the
+                                      table (for existing tokens) must be < num_pages */
+  const int32_t* page_table_dev;   /* DEVICE [num_seqs, max_pages_per_seq]            */
+  int32_t qk_dtype;                /* fp_dtype of q and k_cache                       */
+  int32_t v_dtype;                 /* fp_dtype of v_cache                              */
+  int32_t out_dtype;               /* FP_F32 or FP_BF16                               */
+  const float* q_scale_dev;        /* DEVICE [Hq]  (qk_dtype == FP_E4M3), else NULL   */
+  const float* k_scale_dev;        /* DEVICE [Hkv] (qk_dtype == FP_E4M3), else NULL   */
+  float softmax_scale;             /* logit scale; <= 0 selects 1/sqrt(head_dim)      */
+} fp_problem;
+
+/* Supported dtype combinations (qk, v): (F32, F32), (BF16, BF16), (E4M3, BF16);
+ * out_dtype F32 or BF16 with any of them.  Longest sequence <= 8192 blocks. */
+
+/* ---- size queries (host only, read cu_seqlens_host) -------------------- */
+int64_t fp_num_blocks(const fp_problem* p);     /* N = sum_s n_s            */
+int32_t fp_max_blocks(const fp_problem* p);     /* n_max                    */
+int64_t fp_num_rows(const fp_problem* p);       /* Hkv * N (CSR rows)       */
+int64_t fp_scores_elems(const fp_problem* p);   /* Hkv * N * n_max          */
+int64_t fp_csr_capacity(const fp_problem* p);   /* Hkv * sum_s n_s (n_s + 1) / 2,
+                                                   every causal block kept   */
+size_t fp_workspace_bytes(const fp_problem* p, int32_t which);
+const char* fp_status_string(int32_t status);
+const char* fp_last_error(void);
+
+/*
+ * fp_discover -- block pooling and pooled block scores.
+ *
+ * Pooling (FlashPrefill summary "长上下文加速 28 倍", 3.1 key pooling; V2 paper
+ * reading 4.1): k_mean[h][boff_s + J] = mean of the keys of block J of
+ * sequence s for KV head h (n_J = tokens actually in the block); v_mean the
+ * same for values.
+ *
+ * Scores (same summary, 3.1 query pooling + global re-weighting): for KV head
+ * h and query block I, let rows(I) be every (query head of h's group, token
+ * of block I) and x_rJ = softmax_scale * q_r . kbar_J for J <= I.  Then
+ *     block_scores[h][boff_s + I][J] = M_IJ + ln S_IJ,
+ *     M_IJ = max_r x_rJ,  S_IJ = sum_r exp(x_rJ - M_IJ),
+ * the log of the max-normalised exp-sum.  Re-weighting a row against its top
+ * block is a subtraction of max_J of this value (done by fp_select).
+ * Entries with J > I are left unspecified.
+ *
+ * The dot products run on bf16 MFMA with kbar rounded to bf16; the result
+ * therefore carries an absolute error of a few 1e-3 (natural-log units),
+ * which fp_select accounts for.
+ *
+ * q, k_cache, v_cache: inputs (layouts above).  k_mean, v_mean, block_scores:
+ * outputs.  ws: FP_WS_DISCOVER workspace.
+ */
+int fp_discover(const fp_problem* p, const void* q, const void* k_cache,
+                const void* v_cache, float* k_mean, float* v_mean,
+                float* block_scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp_select -- max-based dynamic threshold, forced blocks, compaction.
+ *
+ * Row (h, s, I) keeps block J <= I iff
+ *     J < ceil(sink_tokens / 128)                 (attention sinks), or
+ *     I - J < max(1, ceil(local_tokens / 128))    (local window; the diagonal
+ *                                                  block is always kept), or
+ *     exp(L_IJ - max_{J' <= I} L_IJ') >= alpha    (threshold alpha * max score,
+ *                                                  FlashPrefill summary 3.2)
+ * where L = block_scores.  alpha <= 0 keeps every causal block.
+ * Kept indices are written ascending (compaction, same summary 3.3).
+ *
+ * Because block_scores comes from a bf16 fast path, every entry whose fast
+ * value lies within 0.05 (natural-log units) of the threshold, together
+ * with the row's candidates for the maximum, is re-evaluated from q and
+ * k_mean in float64 before it is decided; all other decisions have a margin
+ * far larger than the fast path's error.
+ *
+ * q, k_mean, block_scores: inputs from the same problem.  row_ptr
+ * [fp_num_rows + 1], col_idx [col_capacity]: outputs.  col_capacity must be
+ * >= fp_csr_capacity(p).  ws: FP_WS_SELECT workspace.
+ */
+int fp_select(const fp_problem* p, const void* q, const float* k_mean,
+              const float* block_scores, float alpha, int32_t sink_tokens,
+              int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx,
+              int64_t col_capacity, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp_sparse_attn_paged -- sparse causal attention over the listed blocks with
+ * block-mean correction.
+ *
+ * For query head hq, token at position p of block I of sequence s, and the
+ * list K(h, s, I) = col_idx[row_ptr[r] .. row_ptr[r+1]) of row r = (h, s, I):
+ *   E = { tokens j <= p of the listed blocks },  y_j = softmax_scale * q . k_j
+ *   C = { J <= I not listed } if mean_correction, else empty,
+ *       z_J = softmax_scale * q . kbar_J + ln n_J,  value vbar_J
+ *   out = (sum_E e^{y_j} v_j + sum_C e^{z_J} vbar_J) / (sum_E e^{y_j} + sum_C e^{z_J})
+ *   lse = ln(sum_E e^{y_j} + sum_C e^{z_J})
+ * (V2 paper reading 4.1: each pruned block contributes n_J e^{q.kbar} vbar to
+ * the numerator and n_J e^{q.kbar} to the denominator.)  Every list must
+ * contain its diagonal block I; listed blocks must be < n_s, ascending.
+ *
+ * The g = Hq / Hkv query heads of a KV head are packed into shared K/V tiles
+ * (PackGQA, V2 paper reading 4.2(1)); K/V tiles are gathered through the page
+ * table without a contiguous copy (4.3).  QK^T runs on bf16 MFMA (fp8 e4m3
+ * MFMA when qk_dtype == FP_E4M3), PV on bf16 MFMA; softmax in fp32.
+ *
+ * q, k_cache, v_cache, row_ptr, col_idx, k_mean, v_mean: inputs (k_mean /
+ * v_mean may be NULL when mean_correction == 0).  out: output.  lse: output
+ * or NULL.  ws: FP_WS_ATTN workspace.
+ */
+int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* row_ptr,
+                         const int32_t* col_idx, const float* k_mean,
+                         const float* v_mean, int32_t mean_correction, void* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHPREFILL_H */

@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function declared in include/flashprefill.h, answers size queries and
+rejects invalid descriptors with the documented status codes before any
+device work."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashprefill.h")
+
+
+@pytest.fixture(scope="module")
+def bind():
+    import block_sparse_long_kpool_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libflashprefill.so is not built (run __graft_entry__.build())")
+    m.load_library()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("fp_discover", "fp_select", "fp_sparse_attn_paged"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(bind):
+    lib = ctypes.CDLL(bind.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(bind.EXPORTED) == declared_functions()
+
+
+def _problem(bind, seqlens=(300, 129, 1), hq=8, hkv=2, page=16, qk="bf16", v="bf16",
+             out="bf16", **kw):
+    import torch
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    maxp = max(1, -(-max(seqlens) // page))
+    table = torch.zeros((len(seqlens), maxp), dtype=torch.int32)
+    return bind.Problem(cu.tolist(), hq, hkv, table, page, 1000, qk, v, out,
+                        cu_seqlens_dev=torch.from_numpy(cu), **kw)
+
+
+def test_size_queries(bind):
+    p = _problem(bind, seqlens=(300, 129, 1, 1000))
+    n = [3, 2, 1, 8]
+    assert p.num_blocks == sum(n)
+    assert p.max_blocks == 8
+    assert p.num_rows == 2 * sum(n)
+    assert p.scores_elems == 2 * sum(n) * 8
+    assert p.csr_capacity == 2 * sum(x * (x + 1) // 2 for x in n)
+    for which in (bind.FP_WS_DISCOVER, bind.FP_WS_SELECT, bind.FP_WS_ATTN):
+        assert p.workspace_bytes(which) > 0
+        assert p.workspace_bytes(which) % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=6, hkv=4), -1),                 # Hq not a multiple of Hkv
+    (dict(page=48), -2),                     # page size neither divides nor is a multiple of 128
+    (dict(qk="e4m3", v="bf16"), -1),         # e4m3 without scales
+    (dict(qk="bf16", v="f32"), -2),          # unsupported dtype combination
+    (dict(hq=34, hkv=2), -2),                # group of 17 heads
+])
+def test_invalid_descriptors_are_rejected(bind, kw, status):
+    p = _problem(bind, **kw)
+    with pytest.raises(bind.FpError) as e:
+        _ = p.num_blocks
+    lib = bind.load_library()
+    # the calls themselves return the same status without touching the device
+    st = lib.fp_discover(p.ref, 1, 1, 1, 1, 1, 1, 256, 1 << 20, None)
+    assert st == status, lib.fp_last_error()
+    assert lib.fp_last_error()
+
+
+def test_null_pointers_and_small_workspace_are_rejected(bind):
+    p = _problem(bind)
+    lib = bind.load_library()
+    assert lib.fp_discover(p.ref, None, 1, 1, 1, 1, 1, 256, 1 << 30, None) == bind.FpError(-1, "").status
+    need = p.workspace_bytes(bind.FP_WS_DISCOVER)
+    assert lib.fp_discover(p.ref, 1, 1, 1, 1, 1, 1, 256, need - 1, None) == -3
+    assert lib.fp_select(p.ref, 1, 1, 1, 0.1, 256, 512, 1, 1, p.csr_capacity - 1, 256,
+                         1 << 30, None) == -4
+    assert lib.fp_select(p.ref, 1, 1, 1, float("nan"), 256, 512, 1, 1, p.csr_capacity, 256,
+                         1 << 30, None) == -1
+    assert lib.fp_sparse_attn_paged(p.ref, 1, 1, 1, 1, 1, None, None, 1, 1, None, 256,
+                                    1 << 30, None) == -1
+    assert lib.fp_status_string(-3) == b"workspace too small"
