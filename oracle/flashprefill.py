@@ -333,7 +333,7 @@ def attend_block(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
 def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
                  local_tokens: int = 512, correction: bool = True,
                  rows: Optional[Sequence] = None, attend: bool = True,
-                 given_csr: Optional[tuple] = None) -> dict:
+                 given_csr: Optional[tuple] = None, cache: Optional[dict] = None) -> dict:
     """Run pool -> score -> select -> attend.
 
     rows: optional list of (h, s, I) to evaluate (default: all).  For each
@@ -342,6 +342,8 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
     given_csr: optional (row_ptr, col_idx) in the library's row order
     (h, global block); when set, attention uses those lists instead of the
     oracle's own selection (to compare attention alone).
+    cache: optional dict kept by the caller between calls; it holds the
+    decoded keys/values and pooled blocks of the last (sequence, kv head).
     """
     B = prob.block_size
     boff = prob.block_offsets()
@@ -349,7 +351,8 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
     if rows is None:
         rows = [(h, s, I) for h in range(prob.hkv) for s in range(prob.num_seqs)
                 for I in range(prob.nblocks(s))]
-    cache = {}
+    if cache is None:
+        cache = {}
 
     def seq_data(s, h):
         key = (s, h)

@@ -7,6 +7,7 @@ module that both the fp64 oracle tests and the GPU path import.
 """
 
 from .workloads import (  # noqa: F401
+    ALPHA_SWEEP,
     CONFIGS,
     Workload,
     WorkloadSpec,
