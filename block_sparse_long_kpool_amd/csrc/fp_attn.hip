@@ -12,29 +12,40 @@
 //   * workgroup = 4 waves = 256 query rows = 2 heads of one GQA group x the
 //     128 tokens of one query block; wave w owns head 2*pack + w/2, tokens
 //     64*(w%2) .. +63 as two 32-row chunks.  The g/2 workgroups of a group
-//     are given consecutive ids on the same XCD so their K/V reads share L2.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (or the 32x32x64 OCP-fp8 MFMA
-//     for e4m3 Q/K): A = K from LDS, B = Q^T held in registers for the whole
+//     get consecutive ids on the same XCD so their K/V reads share that L2.
+//   * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no staging
+//     registers): every lane gathers 16 bytes of a token row through the page
+//     table and the hardware writes lane i's bytes at LDS base + 16 i.  Rows
+//     are unpadded and 16-byte chunks are XOR-swizzled by row (swz16 /
+//     swz8), which makes the MFMA operand reads below conflict-free.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (the OCP-fp8 32x32x64 MFMA for
+//     e4m3 Q/K): A = K from LDS, B = Q^T held in registers for the whole
 //     kernel.  In the result layout each lane owns one query row and 16 keys
 //     per 32-key chunk, so the online softmax is lane-local plus one l^32
-//     exchange.
+//     exchange; the running max is only raised when it grows by more than
+//     64 (log2 units), so tiles almost never rescale the output accumulator.
 //   * O^T = V^T P^T: B = P^T comes straight from the lane's own softmax
 //     registers; A = V^T is read from the natural [key][d] LDS tile with
 //     ds_read_b64_tr_b16 (16x4 transposes inside 16-lane groups).
-//   * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//     issued before the current tile's math.
 //   * correction tiles: 128 pooled keys/values (bf16) per tile with a
 //     log2(n_J) bias; listed blocks and J > I are masked to -inf.
+#include <type_traits>
+
 #include "fp_internal.hpp"
 
 namespace fp {
 
 namespace {
 
-constexpr int kStride = kHeadDim + 8;       // bf16 elements per LDS row (272 B)
-constexpr int kStride8 = kHeadDim + 16;     // bytes per LDS row of an fp8 K tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Tolerated growth of the running max (log2 units) before the output
+// accumulator is rescaled.  Probabilities are formed as 2^(y - m) with a max m
+// that may lag the true one by up to kLazy, i.e. values up to 2^64: far inside
+// the bf16 / fp32 exponent range, and relative precision does not depend on
+// magnitude.  In practice the rescale then runs at most once per row.
+constexpr float kLazy = 64.0f;
+constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
 
 struct AttnArgs {
   const int32_t* cu;
@@ -60,18 +71,55 @@ struct AttnArgs {
 };
 
 struct SharedMem {
-  u16 k[2][kBlock * kStride];
-  u16 v[2][kBlock * kStride];
+  u16 k[2][kTileElems];  // fp8 tiles use the first half of a buffer
+  u16 v[2][kTileElems];
   float bias[2][kBlock];
+  int slot[2][kBlock];  // cache slot (page * page_size + offset) of each token row of a kept tile
   uint32_t kept_bits[kMaxBlocksPerSeq / 32];
   int pooled_list[kMaxBlocksPerSeq / kBlock];
   int npooled;
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS has 64 banks of 4 bytes (256 bytes per row of banks).  Physical 16-byte
+// chunk of logical chunk c in row r of a 256-byte bf16 row: c ^ g(r & 15),
+// g swapping the two 2-bit halves of the row index.  Then (a) 16 consecutive
+// rows read at one logical chunk (the K operand) hit 16 different chunks, and
+// (b) 4 consecutive rows x 4 consecutive chunks (the V^T transposed reads of a
+// 32-lane half) hit 16 different chunks: both patterns are conflict-free.
+__device__ __forceinline__ int swz16(int c, int r) { return c ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
+// 128-byte fp8 rows (8 chunks, two rows per bank row): chunk c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz8(int c, int r) { return c ^ ((r >> 1) & 7); }
+
 __device__ __forceinline__ bf16x4 lds_read_tr(const u16* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(const_cast<u16*>(p)));
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(const_cast<u16*>(p)));
   return __builtin_bit_cast(bf16x4, r);
+}
+
+// In-place scale of an MFMA accumulator held in AGPRs (VALU instructions
+// cannot read AGPRs, so each element goes AGPR -> VGPR -> multiply -> AGPR);
+// the "+a" constraint keeps the accumulator in accumulation registers.
+__device__ __forceinline__ void scale_acc(f32x16& x, float c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float e = x[i];
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32_e32 %1, %2, %1\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(e), "=&v"(t)
+        : "v"(c));
+    x[i] = e;
+  }
 }
 
 __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
@@ -80,144 +128,12 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
   return uint2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
-// Tile staging.  A tile is either a kept key block J of the sequence (gathered
-// from the paged cache) or a pooled tile pt (bf16 kbar/vbar rows 128pt..+127).
-// PREFETCH: global loads go to registers first (stage_load) and are written
-// to LDS after the current tile's math (stage_store); fp32 caches are loaded
-// and converted synchronously inside stage_store instead.
-template <int QDT, int VDT>
-struct Stager {
-  static constexpr bool kPrefetch = QDT != FP_F32;
-  uint4 kr[8];
-  uint4 vr[8];
-
-  __device__ __forceinline__ void load(const AttnArgs& a, int s, int h, int len, int64_t pooled_base,
-                                       bool pooled, int idx, int I) {
-    if constexpr (!kPrefetch) return;
-    const int tid = threadIdx.x;
-    if (pooled) {
-      // only pooled rows J <= I exist for this query block
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int c = it * 256 + tid, key = c >> 4, part = c & 15;
-        const int J = idx * kBlock + key;
-        uint4 kx = uint4{0, 0, 0, 0}, vx = uint4{0, 0, 0, 0};
-        if (J <= I) {
-          const int64_t off = (pooled_base + J) * kHeadDim + part * 8;
-          kx = *reinterpret_cast<const uint4*>(a.km16 + off);
-          vx = *reinterpret_cast<const uint4*>(a.vm16 + off);
-        }
-        kr[it] = kx;
-        vr[it] = vx;
-      }
-      return;
-    }
-    const int64_t ptrow = (int64_t)s * a.max_pages;
-    // K
-    if constexpr (QDT == FP_E4M3) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int c = it * 256 + tid, key = c >> 3, part = c & 7;
-        const int p = idx * kBlock + key;
-        uint4 r = uint4{0, 0, 0, 0};
-        if (p < len) {
-          const int page = a.page_table[ptrow + p / a.page_size];
-          const int64_t e = (((int64_t)page * a.page_size + p % a.page_size) * a.hkv + h) * kHeadDim + part * 16;
-          r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.k_cache) + e);
-        }
-        kr[it] = r;
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int c = it * 256 + tid, key = c >> 4, part = c & 15;
-        const int p = idx * kBlock + key;
-        uint4 r = uint4{0, 0, 0, 0};
-        if (p < len) {
-          const int page = a.page_table[ptrow + p / a.page_size];
-          const int64_t e = (((int64_t)page * a.page_size + p % a.page_size) * a.hkv + h) * kHeadDim + part * 8;
-          r = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(a.k_cache) + e);
-        }
-        kr[it] = r;
-      }
-    }
-    // V (bf16)
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = it * 256 + tid, key = c >> 4, part = c & 15;
-      const int p = idx * kBlock + key;
-      uint4 r = uint4{0, 0, 0, 0};
-      if (p < len) {
-        const int page = a.page_table[ptrow + p / a.page_size];
-        const int64_t e = (((int64_t)page * a.page_size + p % a.page_size) * a.hkv + h) * kHeadDim + part * 8;
-        r = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(a.v_cache) + e);
-      }
-      vr[it] = r;
-    }
-  }
-
-  __device__ __forceinline__ void store(const AttnArgs& a, SharedMem& sm, int buf, int s, int h,
-                                        int len, int64_t pooled_base, bool pooled, int idx, int I) {
-    const int tid = threadIdx.x;
-    if (pooled && tid < kBlock) {
-      const int J = idx * kBlock + tid;
-      const bool kept = (sm.kept_bits[J >> 5] >> (J & 31)) & 1u;
-      const int nJ = min(kBlock, len - J * kBlock);
-      sm.bias[buf][tid] = (J <= I && !kept) ? __log2f((float)nJ) : -INFINITY;
-    }
-    if constexpr (kPrefetch) {
-      if (pooled || QDT == FP_BF16) {
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int c = it * 256 + tid, key = c >> 4, part = c & 15;
-          *reinterpret_cast<uint4*>(&sm.k[buf][key * kStride + part * 8]) = kr[it];
-        }
-      } else {
-        uint8_t* kb = reinterpret_cast<uint8_t*>(sm.k[buf]);
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int c = it * 256 + tid, key = c >> 3, part = c & 7;
-          *reinterpret_cast<uint4*>(kb + key * kStride8 + part * 16) = kr[it];
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int c = it * 256 + tid, key = c >> 4, part = c & 15;
-        *reinterpret_cast<uint4*>(&sm.v[buf][key * kStride + part * 8]) = vr[it];
-      }
-    } else {
-      // fp32 caches (and their pooled tiles): load, round to bf16, store.
-      const int64_t ptrow = (int64_t)s * a.max_pages;
-      for (int it = 0; it < 16; ++it) {
-        const int c = it * 256 + tid, key = c >> 5, part = c & 31;
-        uint2 kw = uint2{0, 0}, vw = uint2{0, 0};
-        if (pooled) {
-          const int J = idx * kBlock + key;
-          if (J <= I) {
-            const int64_t off = (pooled_base + J) * kHeadDim + part * 4;
-            kw = *reinterpret_cast<const uint2*>(a.km16 + off);
-            vw = *reinterpret_cast<const uint2*>(a.vm16 + off);
-          }
-        } else {
-          const int p = idx * kBlock + key;
-          if (p < len) {
-            const int page = a.page_table[ptrow + p / a.page_size];
-            const int64_t e = (((int64_t)page * a.page_size + p % a.page_size) * a.hkv + h) * kHeadDim + part * 4;
-            kw = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.k_cache) + e));
-            vw = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.v_cache) + e));
-          }
-        }
-        *reinterpret_cast<uint2*>(&sm.k[buf][key * kStride + part * 4]) = kw;
-        *reinterpret_cast<uint2*>(&sm.v[buf][key * kStride + part * 4]) = vw;
-      }
-    }
-  }
-};
-
 template <int QDT, int VDT, int ODT>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SharedMem& sm = *reinterpret_cast<SharedMem*>(smem_raw);
+  constexpr bool kFp8 = QDT == FP_E4M3;
+  constexpr bool kF32 = QDT == FP_F32;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,6 +160,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int64_t pooled_base = (int64_t)h * a.num_blocks + a.boff[s];
   const int kbeg = a.row_ptr[row];
   const int nkept = a.row_ptr[row + 1] - kbeg;
+  const int64_t ptrow = (int64_t)s * a.max_pages;
 
   const int hh = 2 * pack + (wave >> 1);
   const bool head_ok = hh < a.group;
@@ -287,9 +204,114 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int npooled = a.correction ? sm.npooled : 0;
   const int ntiles = nkept + npooled;
 
+  // ---- tile staging -------------------------------------------------------
+  // Kept block J: token rows J*128 .. +127 of the sequence (rows past the end
+  // of the sequence re-read the block's first token: finite values that the
+  // causal mask removes).  Pooled tile pt: pooled rows pt*128 .. +127 of the
+  // sequence (rows past I re-read row I; their bias is -inf).
+  //
+  // Page-table lookups run one tile ahead of the K/V gathers: threads 0..127
+  // fetch the page of row `tid` of tile t+2 while tile t is computed and
+  // publish the cache slot in sm.slot, so the gathers of tile t+1 never wait
+  // on a dependent load.  Page sizes that divide 128 are powers of two
+  // (shift / mask); larger ones are multiples of 128 (one page per block).
+  const int psz = a.page_size;
+  const bool small_pages = psz <= kBlock;
+  const int pshift = 31 - __clz(psz);
+  auto tile_index = [&](int t) { return t >= nkept ? sm.pooled_list[t - nkept] : a.col_idx[kbeg + t]; };
+  // page id of row `tid` of kept tile t (only threads < 128); -1 if pooled
+  auto fetch_page = [&](int t) -> int {
+    if (t >= ntiles || t >= nkept || tid >= kBlock) return -1;
+    const int J = a.col_idx[kbeg + t];
+    const int p0 = J * kBlock + tid;
+    const int p = p0 < len ? p0 : J * kBlock;
+    return a.page_table[ptrow + (small_pages ? (p >> pshift) : (p / psz))];
+  };
+  auto publish_slot = [&](int t, int page, int sbuf) {
+    if (t >= ntiles || t >= nkept || tid >= kBlock) return;
+    const int J = a.col_idx[kbeg + t];
+    const int p0 = J * kBlock + tid;
+    const int p = p0 < len ? p0 : J * kBlock;
+    sm.slot[sbuf][tid] = page * psz + (small_pages ? (p & (psz - 1)) : (p % psz));
+  };
+  auto issue_tile = [&](int t, int buf) {
+    const bool pooled = t >= nkept;
+    const int idx = tile_index(t);
+    if (pooled && tid < kBlock) {
+      const int J = idx * kBlock + tid;
+      const bool kept = (sm.kept_bits[J >> 5] >> (J & 31)) & 1u;
+      const int nJ = min(kBlock, len - J * kBlock);
+      sm.bias[buf][tid] = (J <= I && !kept) ? __log2f((float)nJ) : -INFINITY;
+    }
+    const int* slots = sm.slot[buf];
+    if constexpr (kF32) {
+      // fp32 cache: load, round to bf16, store swizzled (no async path)
+      for (int it = 0; it < 8; ++it) {
+        const int c16 = it * 256 + tid;  // 16-byte chunk of the bf16 tile
+        const int r = c16 >> 4, c = c16 & 15;
+        uint4 kw, vw;
+        if (pooled) {
+          const int J = min(idx * kBlock + r, I);
+          kw = *reinterpret_cast<const uint4*>(a.km16 + (pooled_base + J) * kHeadDim + c * 8);
+          vw = *reinterpret_cast<const uint4*>(a.vm16 + (pooled_base + J) * kHeadDim + c * 8);
+        } else {
+          const int64_t e = ((int64_t)slots[r] * a.hkv + h) * kHeadDim + c * 8;
+          const float* ks = reinterpret_cast<const float*>(a.k_cache) + e;
+          const float* vs = reinterpret_cast<const float*>(a.v_cache) + e;
+          const uint2 ka = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(ks));
+          const uint2 kb = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(ks + 4));
+          const uint2 va = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(vs));
+          const uint2 vb = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(vs + 4));
+          kw = uint4{ka.x, ka.y, kb.x, kb.y};
+          vw = uint4{va.x, va.y, vb.x, vb.y};
+        }
+        const int off = r * kHeadDim + swz16(c, r) * 8;
+        *reinterpret_cast<uint4*>(&sm.k[buf][off]) = kw;
+        *reinterpret_cast<uint4*>(&sm.v[buf][off]) = vw;
+      }
+      return;
+    }
+    // bf16 rows: each wave-instruction fills 1 KiB = 4 rows of 256 B
+    const int sub = lane >> 4, pc = lane & 15;
+    if (pooled) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = (wave * 8 + it) * 4 + sub;
+        const int c = swz16(pc, r);
+        const int J = min(idx * kBlock + r, I);
+        const int64_t e = (pooled_base + J) * kHeadDim + c * 8;
+        load_lds16(a.km16 + e, &sm.k[buf][(wave * 8 + it) * 512]);
+        load_lds16(a.vm16 + e, &sm.v[buf][(wave * 8 + it) * 512]);
+      }
+      return;
+    }
+    const u16* vc = reinterpret_cast<const u16*>(a.v_cache);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = (wave * 8 + it) * 4 + sub;
+      const int c = swz16(pc, r);
+      const int64_t tokrow = ((int64_t)slots[r] * a.hkv + h) * kHeadDim;
+      load_lds16(vc + tokrow + c * 8, &sm.v[buf][(wave * 8 + it) * 512]);
+      if constexpr (!kFp8) {
+        load_lds16(reinterpret_cast<const u16*>(a.k_cache) + tokrow + c * 8, &sm.k[buf][(wave * 8 + it) * 512]);
+      }
+    }
+    if constexpr (kFp8) {
+      // fp8 rows of 128 B: each wave-instruction fills 8 rows
+      const int sub8 = lane >> 3, pc8 = lane & 7;
+      uint8_t* kb = reinterpret_cast<uint8_t*>(sm.k[buf]);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = (wave * 4 + it) * 8 + sub8;
+        const int c = swz8(pc8, r);
+        const int64_t tokrow = ((int64_t)slots[r] * a.hkv + h) * kHeadDim;
+        load_lds16(reinterpret_cast<const uint8_t*>(a.k_cache) + tokrow + c * 16, kb + (wave * 4 + it) * 1024);
+      }
+    }
+  };
+
   // ---- Q^T fragments (B operand), kept for the whole kernel ----
   // lane owns row col of chunk rc; head-dim slots 64*half + 8*kk + i
-  constexpr bool kFp8 = QDT == FP_E4M3;
   bf16x8 qf[2][8];
   i32x8 qf8[2][2];
   int nvalid[2];
@@ -310,15 +332,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         }
         qf8[rc][k2] = v;
       }
-      // bf16 copy for the pooled (correction) tiles: exact widening
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int k2 = kk >> 2, w0 = 2 * (kk & 3);
-        const unsigned wlo = (unsigned)qf8[rc][k2][w0], whi = (unsigned)qf8[rc][k2][w0 + 1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          qf[rc][kk][i] = f32_to_bf16(e4m3_to_f32(((i < 4 ? wlo : whi) >> (8 * (i & 3))) & 0xFFu));
-      }
+      for (int kk = 0; kk < 8; ++kk) qf[rc][kk] = bf16x8{};
     } else if constexpr (QDT == FP_BF16) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
@@ -358,128 +373,187 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dc = 0; dc < 4; ++dc) o[rc][dc] = f32x16{};
   }
 
-  auto tile_desc = [&](int t, bool& pooled) -> int {
-    pooled = t >= nkept;
-    return pooled ? sm.pooled_list[t - nkept] : a.col_idx[kbeg + t];
-  };
-
-  Stager<QDT, VDT> stg;
-  if (ntiles > 0) {
-    bool pooled;
-    const int idx = tile_desc(0, pooled);
-    stg.load(a, s, h, len, pooled_base, pooled, idx, I);
-    stg.store(a, sm, 0, s, h, len, pooled_base, pooled, idx, I);
-  }
+  // prologue: slots of tiles 0 and 1, gathers of tile 0
+  publish_slot(0, fetch_page(0), 0);
+  __syncthreads();
+  if (ntiles > 0) issue_tile(0, 0);
+  publish_slot(1, fetch_page(1), 1);
+  wait_vm();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Kept tiles first, then pooled (correction) tiles: two loops over one
+  // iteration body so each loop holds only the Q form it multiplies with
+  // (fp8 codes for kept tiles of fp8 inputs, bf16 otherwise).
+  auto iterate = [&](int t, auto pooled_c) {
+    constexpr bool POOLED_TILE = decltype(pooled_c)::value;
     const int buf = t & 1;
-    bool pooled;
-    const int idx = tile_desc(t, pooled);
-    bool pooled_n = false;
-    int idx_n = 0;
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      idx_n = tile_desc(t + 1, pooled_n);
-      stg.load(a, s, h, len, pooled_base, pooled_n, idx_n, I);
-    }
+    const bool pooled = POOLED_TILE;
+    const int idx = tile_index(t);
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    const int page_next = fetch_page(t + 2);  // consumed after the math below
 
-    // ---- S^T = K Q^T ----
-    f32x16 sacc[2][4];
+    // The 128-key tile is processed as two 64-key halves (kh): QK^T, online
+    // softmax and PV per half keep the live score / probability registers at
+    // 64 + 32 per lane, while every K and V element is still read from LDS
+    // once per wave.
+    // One 64-key half of the tile, specialised (compile time) for kept,
+    // diagonal and pooled tiles so the softmax carries no per-element selects.
+    auto half_step = [&](int kh, auto pooled_c, auto diag_c) {
+      constexpr bool POOLED = decltype(pooled_c)::value;
+      constexpr bool DIAG = decltype(diag_c)::value;
+      // ---- S^T = K Q^T for keys 64 kh .. +63 ----
+      f32x16 sacc[2][2];
 #pragma unroll
-    for (int rc = 0; rc < 2; ++rc)
+      for (int rc = 0; rc < 2; ++rc)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) sacc[rc][kc] = f32x16{};
-    if (kFp8 && !pooled) {
-      const uint8_t* kb = reinterpret_cast<const uint8_t*>(sm.k[buf]);
+        for (int k2c = 0; k2c < 2; ++k2c) sacc[rc][k2c] = f32x16{};
+      if constexpr (kFp8 && !POOLED) {
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(sm.k[buf]);
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+        for (int k2c = 0; k2c < 2; ++k2c) {
+          const int r = (2 * kh + k2c) * 32 + col;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const i32x4* p = reinterpret_cast<const i32x4*>(kb + (kc * 32 + col) * kStride8 + 64 * half + 32 * k2);
-          const i32x4 lo = p[0], hi = p[1];
-          const i32x8 av = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int c0 = 4 * half + 2 * k2;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + r * 128 + swz8(c0, r) * 16);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + r * 128 + swz8(c0 + 1, r) * 16);
+            const i32x8 av = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int rc = 0; rc < 2; ++rc)
-            sacc[rc][kc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, qf8[rc][k2], sacc[rc][kc], 0, 0, 0, 127, 0, 127);
+            for (int rc = 0; rc < 2; ++rc)
+              sacc[rc][k2c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf8[rc][k2], sacc[rc][k2c], 0,
+                                                                              0, 0, 127, 0, 127);
+          }
+        }
+      } else {
+        const u16* kb = sm.k[buf];
+#pragma unroll
+        for (int k2c = 0; k2c < 2; ++k2c) {
+          const int r = (2 * kh + k2c) * 32 + col;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + r * kHeadDim + swz16(8 * half + kk, r) * 8);
+#pragma unroll
+            for (int rc = 0; rc < 2; ++rc)
+              sacc[rc][k2c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[rc][kk], sacc[rc][k2c], 0, 0, 0);
+          }
         }
       }
-    } else {
-      const u16* kb = sm.k[buf];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + (kc * 32 + col) * kStride + 64 * half + 8 * kk);
-#pragma unroll
-          for (int rc = 0; rc < 2; ++rc)
-            sacc[rc][kc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[rc][kk], sacc[rc][kc], 0, 0, 0);
-        }
-      }
-    }
 
-    // ---- online softmax (log2 domain) ----
-    const float cs = pooled ? c_pool : c_kept;
-    const bool diag = !pooled && idx == I;
-    bf16x8 pb[2][8];
+      // ---- online softmax (log2 domain) ----
+      // lane's keys in this half: 64 kh + 32 k2c + 8 j + 4 half + e, slot i = 4 j + e
+      bf16x8 pb[2][4];
+      float corr[2];
+      bool need_rescale = false;
 #pragma unroll
-    for (int rc = 0; rc < 2; ++rc) {
-      const int p_local = tbase + 32 * rc + col;
-      float mloc = -INFINITY;
+      for (int rc = 0; rc < 2; ++rc) {
+        if constexpr (POOLED) {
+          const float cs = c_pool;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+          for (int k2c = 0; k2c < 2; ++k2c)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * kc + 8 * (i >> 2) + 4 * half + (i & 3);
-          float y = sacc[rc][kc][i] * cs;
-          if (pooled) y += sm.bias[buf][key];
-          if (diag && key > p_local) y = -INFINITY;
-          sacc[rc][kc][i] = y;
-          mloc = fmaxf(mloc, y);
+            for (int j = 0; j < 4; ++j) {
+              const float4 bv = *reinterpret_cast<const float4*>(&sm.bias[buf][64 * kh + 32 * k2c + 8 * j + 4 * half]);
+              sacc[rc][k2c][4 * j + 0] = fmaf(sacc[rc][k2c][4 * j + 0], cs, bv.x);
+              sacc[rc][k2c][4 * j + 1] = fmaf(sacc[rc][k2c][4 * j + 1], cs, bv.y);
+              sacc[rc][k2c][4 * j + 2] = fmaf(sacc[rc][k2c][4 * j + 2], cs, bv.z);
+              sacc[rc][k2c][4 * j + 3] = fmaf(sacc[rc][k2c][4 * j + 3], cs, bv.w);
+            }
         }
-      }
-      const float mnew = fmaxf(m_run[rc], fmaxf(mloc, __shfl_xor(mloc, 32, 64)));
-      const float corr = __builtin_amdgcn_exp2f(m_run[rc] - mnew);
-      m_run[rc] = mnew;
-      float lsum = 0.f;
+        if constexpr (DIAG) {
+          const int p_local = tbase + 32 * rc + col;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+          for (int k2c = 0; k2c < 2; ++k2c)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pe = __builtin_amdgcn_exp2f(sacc[rc][kc][i] - mnew);
-          lsum += pe;
-          pb[rc][2 * kc + (i >> 3)][i & 7] = f32_to_bf16(pe);
+            for (int i = 0; i < 16; ++i) {
+              const int key = 64 * kh + 32 * k2c + 8 * (i >> 2) + 4 * half + (i & 3);
+              if (key > p_local) sacc[rc][k2c][i] = -INFINITY;
+            }
         }
-      }
-      l_run[rc] = l_run[rc] * corr + lsum;
+        float mloc = sacc[rc][0][0];
 #pragma unroll
-      for (int dc = 0; dc < 4; ++dc) o[rc][dc] *= corr;
-    }
+        for (int k2c = 0; k2c < 2; ++k2c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[rc][k2c][i]);
+        if constexpr (!POOLED) mloc *= c_kept;
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        // lazy max: keep the running max unless this half exceeds it by > kLazy
+        const float m_old = m_run[rc];
+        const float m_use = (mloc > m_old + kLazy) ? mloc : m_old;
+        need_rescale |= m_use != m_old;
+        corr[rc] = __builtin_amdgcn_exp2f(m_old - m_use);
+        m_run[rc] = m_use;
+        float lsum = 0.f;
+#pragma unroll
+        for (int k2c = 0; k2c < 2; ++k2c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float arg;
+            if constexpr (POOLED) arg = sacc[rc][k2c][i] - m_use;
+            else arg = fmaf(sacc[rc][k2c][i], c_kept, -m_use);
+            const float pe = __builtin_amdgcn_exp2f(arg);
+            lsum += pe;
+            pb[rc][2 * k2c + (i >> 3)][i & 7] = f32_to_bf16(pe);
+          }
+        l_run[rc] = l_run[rc] * corr[rc] + lsum;
+      }
+      if (__any(need_rescale)) {
+#pragma unroll
+        for (int rc = 0; rc < 2; ++rc)
+#pragma unroll
+          for (int dc = 0; dc < 4; ++dc) scale_acc(o[rc][dc], corr[rc]);
+      }
 
-    // ---- O^T += V^T P^T ----
-    {
+      // ---- O^T += V^T P^T over keys 64 kh .. +63 ----
       const u16* vb = sm.v[buf];
-      const int vrow = 4 * half + ((lane & 15) >> 2);
-      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const int vrow = 4 * half + ((lane & 15) >> 2);              // + 16 ks (+ 8)
+      const int csel = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dc
+      const int vsub = 4 * (lane & 1);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ksl = 0; ksl < 4; ++ksl) {
+        const int r = 16 * (4 * kh + ksl) + vrow;
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
-          const u16* p = vb + (16 * ks + vrow) * kStride + 32 * dc + vcol;
-          const bf16x4 lo = lds_read_tr(p);
-          const bf16x4 hi = lds_read_tr(p + 8 * kStride);
+          const bf16x4 lo = lds_read_tr(vb + r * kHeadDim + swz16(4 * dc + csel, r) * 8 + vsub);
+          const bf16x4 hi = lds_read_tr(vb + (r + 8) * kHeadDim + swz16(4 * dc + csel, r + 8) * 8 + vsub);
           const bf16x8 av = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int rc = 0; rc < 2; ++rc)
-            o[rc][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rc][ks], o[rc][dc], 0, 0, 0);
+            o[rc][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rc][ksl], o[rc][dc], 0, 0, 0);
         }
+      }
+    };
+
+    const bool diag = !pooled && idx == I;
+#pragma unroll 1
+    for (int kh = 0; kh < 2; ++kh) {
+      if constexpr (POOLED_TILE) {
+        half_step(kh, std::true_type{}, std::false_type{});
+      } else {
+        if (diag) half_step(kh, std::false_type{}, std::true_type{});
+        else half_step(kh, std::false_type{}, std::false_type{});
       }
     }
 
-    if (more) stg.store(a, sm, buf ^ 1, s, h, len, pooled_base, pooled_n, idx_n, I);
+    publish_slot(t + 2, page_next, buf);
+    wait_vm();
     __syncthreads();
+  };
+
+  for (int t = 0; t < nkept; ++t) iterate(t, std::false_type{});
+  if constexpr (kFp8) {
+    // pooled tiles run on bf16 MFMA: widen the fp8 Q fragments (exact)
+#pragma unroll
+    for (int rc = 0; rc < 2; ++rc)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int k2 = kk >> 2, w0 = 2 * (kk & 3);
+        const unsigned wlo = (unsigned)qf8[rc][k2][w0], whi = (unsigned)qf8[rc][k2][w0 + 1];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          qf[rc][kk][i] = f32_to_bf16(e4m3_to_f32(((i < 4 ? wlo : whi) >> (8 * (i & 3))) & 0xFFu));
+      }
   }
+  for (int t = nkept; t < ntiles; ++t) iterate(t, std::true_type{});
 
   // ---- epilogue: O = acc / l, lse = m + log2(l) (natural log out) ----
 #pragma unroll
@@ -508,13 +582,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// boff (block 0 of the grid) and bf16 copies of the pooled keys / values.
+// boff (last block of the grid) and bf16 copies of the pooled keys / values.
 __global__ __launch_bounds__(256) void attn_prep_kernel(const int32_t* __restrict__ cu, int num_seqs,
                                                         int32_t* __restrict__ boff, const float* __restrict__ km,
                                                         const float* __restrict__ vm, u16* __restrict__ km16,
                                                         u16* __restrict__ vm16, int64_t n) {
   if (blockIdx.x == gridDim.x - 1) {
-    // sequential-in-chunks scan of ceil(len/128): one block
     __shared__ int buf[256];
     __shared__ int carry;
     if (threadIdx.x == 0) carry = 0;
@@ -579,6 +652,7 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   a.out = out;
   a.lse = lse;
   a.num_blocks = g.num_blocks;
+  a.total_tokens = g.total_tokens;
   a.num_seqs = g.num_seqs;
   a.max_pages = g.max_pages;
   a.page_size = g.page_size;
@@ -588,7 +662,6 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   a.packs = (g.group + 1) / 2;
   a.correction = correction;
   a.softmax_scale = g.softmax_scale;
-  a.total_tokens = g.total_tokens;
   const int64_t rows = (int64_t)g.hkv * g.num_blocks;
   const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs);
   const size_t shm = sizeof(SharedMem);
