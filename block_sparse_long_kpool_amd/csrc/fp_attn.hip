@@ -46,6 +46,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // magnitude.  In practice the rescale then runs at most once per row.
 constexpr float kLazy = 64.0f;
 constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
+#ifndef FP_ATTN_WAVES
+#define FP_ATTN_WAVES 8
+#endif
+// waves per workgroup: 8 = two waves per SIMD, 32 query rows each
+constexpr int kAttnWaves = FP_ATTN_WAVES;
 
 struct AttnArgs {
   const int32_t* cu;
@@ -128,8 +133,10 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
   return uint2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
-template <int QDT, int VDT, int ODT>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+template <int QDT, int VDT, int ODT, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
+  constexpr int RC = 8 / NW;   // 32-row chunks per wave (the workgroup always covers 256 rows)
+  constexpr int NT = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SharedMem& sm = *reinterpret_cast<SharedMem*>(smem_raw);
   constexpr bool kFp8 = QDT == FP_E4M3;
@@ -162,17 +169,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int nkept = a.row_ptr[row + 1] - kbeg;
   const int64_t ptrow = (int64_t)s * a.max_pages;
 
-  const int hh = 2 * pack + (wave >> 1);
+  const int hh = 2 * pack + (wave * RC) / 4;
   const bool head_ok = hh < a.group;
   const int hq_idx = h * a.group + (head_ok ? hh : 0);
-  const int tbase = 64 * (wave & 1);
+  const int tbase = 32 * ((wave * RC) % 4);
 
   // ---- kept-block bitmap and the pooled tiles that hold a pruned block ----
   const int nwords = (I >> 5) + 1;
   if (a.correction) {
-    for (int w = tid; w < nwords; w += 256) sm.kept_bits[w] = 0u;
+    for (int w = tid; w < nwords; w += NT) sm.kept_bits[w] = 0u;
     __syncthreads();
-    for (int i = tid; i < nkept; i += 256) {
+    for (int i = tid; i < nkept; i += NT) {
       const int J = a.col_idx[kbeg + i];
       if ((unsigned)J <= (unsigned)I) atomicOr(&sm.kept_bits[J >> 5], 1u << (J & 31));
     }
@@ -246,8 +253,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int* slots = sm.slot[buf];
     if constexpr (kF32) {
       // fp32 cache: load, round to bf16, store swizzled (no async path)
-      for (int it = 0; it < 8; ++it) {
-        const int c16 = it * 256 + tid;  // 16-byte chunk of the bf16 tile
+      for (int it = 0; it < 2048 / NT; ++it) {
+        const int c16 = it * NT + tid;  // 16-byte chunk of the bf16 tile
         const int r = c16 >> 4, c = c16 & 15;
         uint4 kw, vw;
         if (pooled) {
@@ -275,25 +282,27 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int sub = lane >> 4, pc = lane & 15;
     if (pooled) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int r = (wave * 8 + it) * 4 + sub;
+      for (int it = 0; it < 32 / NW; ++it) {
+        const int wi = wave * (32 / NW) + it;  // wave-instruction index: 1 KiB of the tile
+        const int r = wi * 4 + sub;
         const int c = swz16(pc, r);
         const int J = min(idx * kBlock + r, I);
         const int64_t e = (pooled_base + J) * kHeadDim + c * 8;
-        load_lds16(a.km16 + e, &sm.k[buf][(wave * 8 + it) * 512]);
-        load_lds16(a.vm16 + e, &sm.v[buf][(wave * 8 + it) * 512]);
+        load_lds16(a.km16 + e, &sm.k[buf][wi * 512]);
+        load_lds16(a.vm16 + e, &sm.v[buf][wi * 512]);
       }
       return;
     }
     const u16* vc = reinterpret_cast<const u16*>(a.v_cache);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = (wave * 8 + it) * 4 + sub;
+    for (int it = 0; it < 32 / NW; ++it) {
+      const int wi = wave * (32 / NW) + it;
+      const int r = wi * 4 + sub;
       const int c = swz16(pc, r);
       const int64_t tokrow = ((int64_t)slots[r] * a.hkv + h) * kHeadDim;
-      load_lds16(vc + tokrow + c * 8, &sm.v[buf][(wave * 8 + it) * 512]);
+      load_lds16(vc + tokrow + c * 8, &sm.v[buf][wi * 512]);
       if constexpr (!kFp8) {
-        load_lds16(reinterpret_cast<const u16*>(a.k_cache) + tokrow + c * 8, &sm.k[buf][(wave * 8 + it) * 512]);
+        load_lds16(reinterpret_cast<const u16*>(a.k_cache) + tokrow + c * 8, &sm.k[buf][wi * 512]);
       }
     }
     if constexpr (kFp8) {
@@ -301,22 +310,23 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const int sub8 = lane >> 3, pc8 = lane & 7;
       uint8_t* kb = reinterpret_cast<uint8_t*>(sm.k[buf]);
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = (wave * 4 + it) * 8 + sub8;
+      for (int it = 0; it < 16 / NW; ++it) {
+        const int wi = wave * (16 / NW) + it;
+        const int r = wi * 8 + sub8;
         const int c = swz8(pc8, r);
         const int64_t tokrow = ((int64_t)slots[r] * a.hkv + h) * kHeadDim;
-        load_lds16(reinterpret_cast<const uint8_t*>(a.k_cache) + tokrow + c * 16, kb + (wave * 4 + it) * 1024);
+        load_lds16(reinterpret_cast<const uint8_t*>(a.k_cache) + tokrow + c * 16, kb + wi * 1024);
       }
     }
   };
 
   // ---- Q^T fragments (B operand), kept for the whole kernel ----
   // lane owns row col of chunk rc; head-dim slots 64*half + 8*kk + i
-  bf16x8 qf[2][8];
-  i32x8 qf8[2][2];
-  int nvalid[2];
+  bf16x8 qf[RC][8];
+  i32x8 qf8[RC][2];
+  int nvalid[RC];
 #pragma unroll
-  for (int rc = 0; rc < 2; ++rc) {
+  for (int rc = 0; rc < RC; ++rc) {
     const int t0 = tbase + 32 * rc;
     nvalid[rc] = head_ok ? max(0, min(32, nI - t0)) : 0;
     const bool rvalid = col < nvalid[rc];
@@ -363,10 +373,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 
   // ---- online-softmax state ----
-  f32x16 o[2][4];
-  float m_run[2], l_run[2];
+  f32x16 o[RC][4];
+  float m_run[RC], l_run[RC];
 #pragma unroll
-  for (int rc = 0; rc < 2; ++rc) {
+  for (int rc = 0; rc < RC; ++rc) {
     m_run[rc] = -INFINITY;
     l_run[rc] = 0.f;
 #pragma unroll
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // Kept tiles first, then pooled (correction) tiles: two loops over one
   // iteration body so each loop holds only the Q form it multiplies with
   // (fp8 codes for kept tiles of fp8 inputs, bf16 otherwise).
-  auto iterate = [&](int t, auto pooled_c) {
+  auto iterate = [&](int t, auto pooled_c, auto diag_c) {
     constexpr bool POOLED_TILE = decltype(pooled_c)::value;
     const int buf = t & 1;
     const bool pooled = POOLED_TILE;
@@ -402,9 +412,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       constexpr bool POOLED = decltype(pooled_c)::value;
       constexpr bool DIAG = decltype(diag_c)::value;
       // ---- S^T = K Q^T for keys 64 kh .. +63 ----
-      f32x16 sacc[2][2];
+      f32x16 sacc[RC][2];
 #pragma unroll
-      for (int rc = 0; rc < 2; ++rc)
+      for (int rc = 0; rc < RC; ++rc)
 #pragma unroll
         for (int k2c = 0; k2c < 2; ++k2c) sacc[rc][k2c] = f32x16{};
       if constexpr (kFp8 && !POOLED) {
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + r * 128 + swz8(c0 + 1, r) * 16);
             const i32x8 av = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-            for (int rc = 0; rc < 2; ++rc)
+            for (int rc = 0; rc < RC; ++rc)
               sacc[rc][k2c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf8[rc][k2], sacc[rc][k2c], 0,
                                                                               0, 0, 127, 0, 127);
           }
@@ -433,7 +443,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           for (int kk = 0; kk < 8; ++kk) {
             const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + r * kHeadDim + swz16(8 * half + kk, r) * 8);
 #pragma unroll
-            for (int rc = 0; rc < 2; ++rc)
+            for (int rc = 0; rc < RC; ++rc)
               sacc[rc][k2c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[rc][kk], sacc[rc][k2c], 0, 0, 0);
           }
         }
@@ -441,11 +451,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
       // ---- online softmax (log2 domain) ----
       // lane's keys in this half: 64 kh + 32 k2c + 8 j + 4 half + e, slot i = 4 j + e
-      bf16x8 pb[2][4];
-      float corr[2];
+      bf16x8 pb[RC][4];
+      float corr[RC];
       bool need_rescale = false;
 #pragma unroll
-      for (int rc = 0; rc < 2; ++rc) {
+      for (int rc = 0; rc < RC; ++rc) {
         if constexpr (POOLED) {
           const float cs = c_pool;
 #pragma unroll
@@ -498,7 +508,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
       if (__any(need_rescale)) {
 #pragma unroll
-        for (int rc = 0; rc < 2; ++rc)
+        for (int rc = 0; rc < RC; ++rc)
 #pragma unroll
           for (int dc = 0; dc < 4; ++dc) scale_acc(o[rc][dc], corr[rc]);
       }
@@ -517,33 +527,30 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           const bf16x4 hi = lds_read_tr(vb + (r + 8) * kHeadDim + swz16(4 * dc + csel, r + 8) * 8 + vsub);
           const bf16x8 av = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int rc = 0; rc < 2; ++rc)
+          for (int rc = 0; rc < RC; ++rc)
             o[rc][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rc][ksl], o[rc][dc], 0, 0, 0);
         }
       }
     };
 
-    const bool diag = !pooled && idx == I;
 #pragma unroll 1
-    for (int kh = 0; kh < 2; ++kh) {
-      if constexpr (POOLED_TILE) {
-        half_step(kh, std::true_type{}, std::false_type{});
-      } else {
-        if (diag) half_step(kh, std::false_type{}, std::true_type{});
-        else half_step(kh, std::false_type{}, std::false_type{});
-      }
-    }
+    for (int kh = 0; kh < 2; ++kh) half_step(kh, pooled_c, diag_c);
 
     publish_slot(t + 2, page_next, buf);
     wait_vm();
     __syncthreads();
   };
 
-  for (int t = 0; t < nkept; ++t) iterate(t, std::false_type{});
+  // lists are ascending and end with the diagonal block: off-diagonal kept
+  // tiles, then the diagonal tile (causal mask), each in a loop of its own
+  const bool last_is_diag = nkept > 0 && tile_index(nkept - 1) == I;
+  const int n_off = last_is_diag ? nkept - 1 : nkept;
+  for (int t = 0; t < n_off; ++t) iterate(t, std::false_type{}, std::false_type{});
+  if (last_is_diag) iterate(nkept - 1, std::false_type{}, std::true_type{});
   if constexpr (kFp8) {
     // pooled tiles run on bf16 MFMA: widen the fp8 Q fragments (exact)
 #pragma unroll
-    for (int rc = 0; rc < 2; ++rc)
+    for (int rc = 0; rc < RC; ++rc)
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int k2 = kk >> 2, w0 = 2 * (kk & 3);
@@ -553,11 +560,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           qf[rc][kk][i] = f32_to_bf16(e4m3_to_f32(((i < 4 ? wlo : whi) >> (8 * (i & 3))) & 0xFFu));
       }
   }
-  for (int t = nkept; t < ntiles; ++t) iterate(t, std::true_type{});
+  for (int t = nkept; t < ntiles; ++t) iterate(t, std::true_type{}, std::false_type{});
 
   // ---- epilogue: O = acc / l, lse = m + log2(l) (natural log out) ----
 #pragma unroll
-  for (int rc = 0; rc < 2; ++rc) {
+  for (int rc = 0; rc < RC; ++rc) {
     const float l_tot = l_run[rc] + __shfl_xor(l_run[rc], 32, 64);
     const float inv = 1.f / l_tot;
     if (col >= nvalid[rc]) continue;
@@ -669,12 +676,12 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   do {                                                                                         \
     static bool attr_set = false;                                                              \
     if (!attr_set) {                                                                           \
-      hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<QD, VD, OD>,                 \
+      hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<QD, VD, OD, kAttnWaves>,     \
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm); \
       if (e != hipSuccess) return e;                                                           \
       attr_set = true;                                                                         \
     }                                                                                          \
-    hipLaunchKernelGGL((attn_kernel<QD, VD, OD>), dim3(grid), dim3(256), shm, st, a);          \
+    hipLaunchKernelGGL((attn_kernel<QD, VD, OD, kAttnWaves>), dim3(grid), dim3(64 * kAttnWaves), shm, st, a); \
   } while (0)
 #define FP_ATTN_O(QD, VD)                                  \
   do {                                                     \
