@@ -79,3 +79,30 @@ def test_gqa_32k_config_sampled_parity():
     w = make_workload(spec_for("gqa_32k"))
     g = run_gpu(w, 0.1)
     compare(w, g, 0.1, rows=sample_rows(w, 6), check_pool=True)
+
+
+@pytest.mark.parametrize("name,nrows", [("sweep_128k", 4), ("varlen_4x", 3), ("long_256k", 3)])
+def test_full_size_config_sampled_parity(name, nrows):
+    """Benchmark-size configs at alpha = 0.1 with correction (the bench launch
+    configuration): pooled means everywhere; lists, scores and outputs on a
+    seeded sample of rows per KV head and sequence (first and last block of
+    every sequence included)."""
+    log(f"case {name}")
+    w = make_workload(spec_for(name))
+    g = run_gpu(w, 0.1)
+    compare(w, g, 0.1, rows=sample_rows(w, nrows), check_pool=True)
+    rp = g["row_ptr"]
+    # structural properties over ALL rows: every list holds its diagonal
+    # block and the forced sink / local blocks, ascending, within range
+    spec = w.spec
+    boff = np.concatenate([[0], np.cumsum([-(-L // 128) for L in spec.seqlens])])
+    ci = g["col_idx"]
+    for h in range(spec.num_kv_heads):
+        for s, L in enumerate(spec.seqlens):
+            n = -(-L // 128)
+            for I in range(n):
+                r = h * int(boff[-1]) + int(boff[s]) + I
+                lst = ci[rp[r]:rp[r + 1]]
+                assert lst[-1] == I and np.all(np.diff(lst) > 0) and lst[0] >= 0
+                assert set(range(min(2, I + 1))) <= set(lst.tolist())
+                assert set(range(max(0, I - 3), I + 1)) <= set(lst.tolist())
