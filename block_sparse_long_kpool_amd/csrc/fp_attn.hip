@@ -9,10 +9,11 @@
 // page table (4.3).
 //
 // gfx950 design:
-//   * workgroup = 4 waves = 256 query rows = 2 heads of one GQA group x the
-//     128 tokens of one query block; wave w owns head 2*pack + w/2, tokens
-//     64*(w%2) .. +63 as two 32-row chunks.  The g/2 workgroups of a group
-//     get consecutive ids on the same XCD so their K/V reads share that L2.
+//   * workgroup = 256 query rows = 2 heads of one GQA group x the 128 tokens
+//     of one query block, split over kAttnWaves waves (8: two waves per SIMD,
+//     one 32-row chunk each; 4: one wave per SIMD, two chunks each).  The g/2
+//     workgroups of a group get consecutive ids on the same XCD so their K/V
+//     reads share that L2.
 //   * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no staging
 //     registers): every lane gathers 16 bytes of a token row through the page
 //     table and the hardware writes lane i's bytes at LDS base + 16 i.  Rows
@@ -85,46 +86,16 @@ struct SharedMem {
   int npooled;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
-
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// LDS has 64 banks of 4 bytes (256 bytes per row of banks).  Physical 16-byte
-// chunk of logical chunk c in row r of a 256-byte bf16 row: c ^ g(r & 15),
-// g swapping the two 2-bit halves of the row index.  Then (a) 16 consecutive
-// rows read at one logical chunk (the K operand) hit 16 different chunks, and
-// (b) 4 consecutive rows x 4 consecutive chunks (the V^T transposed reads of a
-// 32-lane half) hit 16 different chunks: both patterns are conflict-free.
-__device__ __forceinline__ int swz16(int c, int r) { return c ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
-// 128-byte fp8 rows (8 chunks, two rows per bank row): chunk c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int swz8(int c, int r) { return c ^ ((r >> 1) & 7); }
-
 __device__ __forceinline__ bf16x4 lds_read_tr(const u16* p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(const_cast<u16*>(p)));
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// In-place scale of an MFMA accumulator held in AGPRs (VALU instructions
-// cannot read AGPRs, so each element goes AGPR -> VGPR -> multiply -> AGPR);
-// the "+a" constraint keeps the accumulator in accumulation registers.
+// In-place rescale of an output accumulator (runs only when a row's running
+// max grows by more than kLazy).
 __device__ __forceinline__ void scale_acc(f32x16& x, float c) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float e = x[i];
-    float t;
-    asm volatile(
-        "v_accvgpr_read_b32 %1, %0\n\t"
-        "v_mul_f32_e32 %1, %2, %1\n\t"
-        "v_accvgpr_write_b32 %0, %1"
-        : "+a"(e), "=&v"(t)
-        : "v"(c));
-    x[i] = e;
-  }
+  for (int i = 0; i < 16; ++i) x[i] *= c;
 }
 
 __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
@@ -391,6 +362,28 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   wait_vm();
   __syncthreads();
 
+  // Per-lane LDS offsets inside a tile.  Every operand read below touches a
+  // row whose low four bits are fixed per lane (the key column for K, vrow and
+  // vrow + 8 for V), so the row swizzle is loop-invariant: a read is a per-lane
+  // base plus uniform offsets (half-tile, chunk row group), the latter folded
+  // into the instruction's immediate.
+  int koff[8];  // bf16 K: row col, logical chunk 8 half + kk (elements)
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * kHeadDim + swz16(8 * half + kk, col) * 8;
+  int koff8[4];  // fp8 K: row col, logical 16-byte chunks 4 half + 0..3 (bytes)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) koff8[c] = col * 128 + swz8(4 * half + c, col) * 16;
+  // V^T transposed reads: 16-row groups, lane rows vrow and vrow + 8 of each
+  const int vrow = 4 * half + ((lane & 15) >> 2);
+  const int csel = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vsub = 4 * (lane & 1);
+  int voff[4][2];
+#pragma unroll
+  for (int dc = 0; dc < 4; ++dc) {
+    voff[dc][0] = vrow * kHeadDim + swz16(4 * dc + csel, vrow) * 8 + vsub;
+    voff[dc][1] = (vrow + 8) * kHeadDim + swz16(4 * dc + csel, vrow + 8) * 8 + vsub;
+  }
+
   // Kept tiles first, then pooled (correction) tiles: two loops over one
   // iteration body so each loop holds only the Q form it multiplies with
   // (fp8 codes for kept tiles of fp8 inputs, bf16 otherwise).
@@ -418,15 +411,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int k2c = 0; k2c < 2; ++k2c) sacc[rc][k2c] = f32x16{};
       if constexpr (kFp8 && !POOLED) {
-        const uint8_t* kb = reinterpret_cast<const uint8_t*>(sm.k[buf]);
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(sm.k[buf]) + kh * 64 * 128;
 #pragma unroll
         for (int k2c = 0; k2c < 2; ++k2c) {
-          const int r = (2 * kh + k2c) * 32 + col;
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
-            const int c0 = 4 * half + 2 * k2;
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + r * 128 + swz8(c0, r) * 16);
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + r * 128 + swz8(c0 + 1, r) * 16);
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + koff8[2 * k2] + k2c * 32 * 128);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + koff8[2 * k2 + 1] + k2c * 32 * 128);
             const i32x8 av = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
             for (int rc = 0; rc < RC; ++rc)
@@ -435,13 +426,12 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
           }
         }
       } else {
-        const u16* kb = sm.k[buf];
+        const u16* kb = sm.k[buf] + kh * 64 * kHeadDim;
 #pragma unroll
         for (int k2c = 0; k2c < 2; ++k2c) {
-          const int r = (2 * kh + k2c) * 32 + col;
 #pragma unroll
           for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + r * kHeadDim + swz16(8 * half + kk, r) * 8);
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + k2c * 32 * kHeadDim);
 #pragma unroll
             for (int rc = 0; rc < RC; ++rc)
               sacc[rc][k2c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[rc][kk], sacc[rc][k2c], 0, 0, 0);
@@ -514,17 +504,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       }
 
       // ---- O^T += V^T P^T over keys 64 kh .. +63 ----
-      const u16* vb = sm.v[buf];
-      const int vrow = 4 * half + ((lane & 15) >> 2);              // + 16 ks (+ 8)
-      const int csel = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // + 4 dc
-      const int vsub = 4 * (lane & 1);
+      const u16* vb = sm.v[buf] + kh * 64 * kHeadDim;
 #pragma unroll
       for (int ksl = 0; ksl < 4; ++ksl) {
-        const int r = 16 * (4 * kh + ksl) + vrow;
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
-          const bf16x4 lo = lds_read_tr(vb + r * kHeadDim + swz16(4 * dc + csel, r) * 8 + vsub);
-          const bf16x4 hi = lds_read_tr(vb + (r + 8) * kHeadDim + swz16(4 * dc + csel, r + 8) * 8 + vsub);
+          const bf16x4 lo = lds_read_tr(vb + ksl * 16 * kHeadDim + voff[dc][0]);
+          const bf16x4 hi = lds_read_tr(vb + ksl * 16 * kHeadDim + voff[dc][1]);
           const bf16x8 av = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int rc = 0; rc < RC; ++rc)

@@ -76,6 +76,46 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// ---- LDS staging ------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lds is wave-uniform and lane i's bytes land at lds + 16 i.  Completion is
+// tracked by vmcnt only, so wait_vm() must precede the barrier that publishes
+// the data.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS has 64 banks of 4 bytes (256 bytes per row of banks).  Physical 16-byte
+// chunk of logical chunk c in row r of a 256-byte bf16 row: c ^ g(r & 15),
+// g swapping the two 2-bit halves of the row index.  Then (a) 16 consecutive
+// rows read at one logical chunk (an MFMA operand gathered across rows) hit 16
+// different chunks, and (b) 4 consecutive rows x 4 consecutive chunks (the
+// V^T transposed reads of a 32-lane half) hit 16 different chunks: both
+// patterns are conflict-free.  The map is an involution in c and depends on
+// the row only through r & 15.
+__device__ __forceinline__ int swz16(int c, int r) { return c ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
+// 128-byte fp8 rows (8 chunks, two rows per bank row): chunk c ^ ((r >> 1) & 7),
+// again a function of r & 15 only.
+__device__ __forceinline__ int swz8(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// Sum / max of the value held by lanes l and l ^ 32 (v_permlane32_swap
+// exchanges the two 32-lane halves; combining both outputs symmetrically gives
+// the pair result in every lane).
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---- launchers (one per translation unit) ---------------------------------
 
 // Block offsets boff[num_seqs + 1] from cu_seqlens (prefix of ceil(len/128)).

@@ -8,15 +8,25 @@
 //     L_IJ = M_IJ + ln S_IJ,  M_IJ = max_r x_rJ,  S_IJ = sum_r exp(x_rJ - M_IJ)
 // with x_rJ = softmax_scale * q_r . kbar_J.
 //
-// One workgroup (8 waves) owns one (h, I) and ALL its rows, so Q is read from
-// HBM exactly once; the pooled keys of head h (bf16, L2-resident) stream
-// through LDS in tiles of 64.  X = Q . Kbar^T runs on v_mfma_f32_32x32x16_bf16
-// with A = Q (rows) and B = Kbar^T (pooled keys), the pooled keys split into
-// two bf16 terms (hi + lo, two MFMAs into one fp32 accumulator) so the fast
-// logits carry errors of a few 1e-5 only: in the result layout every
-// lane owns one pooled-key column and 16 rows, so the per-column max and
-// exp-sum are lane-local; lanes l and l^32 share a column and the 8 waves are
-// merged through LDS.
+// gfx950 design:
+//   * one workgroup (8 waves) owns one (h, I) and ALL its rows; the rows go
+//     in passes of 8 waves x 2 chunks x 32 rows, each wave holding the Q
+//     fragments of its two chunks in registers for the whole pass, so Q is
+//     read from HBM once (passes = g / 4).
+//   * pooled keys (bf16 hi and lo terms of kbar, L2-resident) stream through
+//     double-buffered LDS in tiles of 128 keys, copied with
+//     global_load_lds_dwordx4 (no staging registers) into XOR-swizzled 256-B
+//     rows, so the MFMA operand reads are conflict-free.
+//   * X = Q . Kbar^T on v_mfma_f32_32x32x16_bf16, hi and lo terms into one
+//     fp32 accumulator (relative residual of the split ~2^-17, so the fast
+//     logits carry errors of a few 1e-5 only).  In the result layout a lane
+//     owns one pooled-key column and 16 rows of each chunk: the column max and
+//     exp-sum are lane-local, lanes l and l^32 are merged with one
+//     v_permlane32_swap each, and the 8 waves through LDS once per tile.
+//   * software pipeline inside a wave: the MFMAs of key chunk j+1 (second
+//     accumulator set) are independent of the max / exp / sum of chunk j, so
+//     the matrix core and the VALU overlap; the logit scale is folded into one
+//     fma per element, and masking runs only for the ragged last block.
 #include "fp_internal.hpp"
 
 namespace fp {
@@ -24,11 +34,31 @@ namespace fp {
 namespace {
 
 constexpr int kWaves = 8;
-constexpr int kJTile = 64;               // pooled keys per LDS tile
-constexpr int kKbStride = kHeadDim + 8;  // bf16 elements per LDS row (272 B)
+constexpr int kRC = 2;                         // 32-row chunks per wave per pass
+constexpr int kChunksPerPass = kWaves * kRC;   // 512 rows per pass
+constexpr int kJT = 128;                       // pooled keys per LDS tile
+constexpr int kJC = kJT / 32;                  // 32-key chunks per tile
+constexpr int kTerm = kJT * kHeadDim;          // bf16 elements of one term of a tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegBig = -1e30f;
+
+struct ScoresSmem {
+  u16 kb[2][2][kTerm];           // [buffer][hi, lo]: 128 KiB
+  float2 part[2][kWaves][kJT];   // per wave (max, sum) of each key, by buffer
+};
+constexpr size_t kScoresSmem = sizeof(ScoresSmem);
+
+struct ScoresArgs {
+  const int32_t* cu;
+  const int32_t* boff;
+  const void* q;
+  const float* q_scale;
+  const u16* kmean16;
+  float* scores;
+  int64_t num_blocks;
+  int num_seqs, hq, hkv, group, max_blocks;
+  float logit_scale;
+};
 
 // Q fragment of one 32-row chunk: lane l holds row l%32, head-dim elements
 // [64*(l/32) + 8*kk, +8) for kk = 0..7 (the MFMA K index is a permutation of
@@ -66,15 +96,117 @@ __device__ __forceinline__ void load_q_frag(const void* q, int64_t row_elem, boo
   }
 }
 
-// RC = 32-row chunks per wave per pass; rows per pass = 8 waves * 32 * RC.
-template <int QDT, int RC>
-__global__ __launch_bounds__(512) void scores_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ boff, int num_seqs, int hq,
-    int hkv, int group, int64_t num_blocks, int max_blocks, float logit_scale,
-    const void* __restrict__ q, const float* __restrict__ q_scale,
-    const u16* __restrict__ kmean16, float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) u16 kb[2][2][kJTile * kKbStride];  // [buf][hi/lo]
-  __shared__ float2 part[2][kWaves][kJTile];
+// X chunk of 32 pooled keys (rows jc*32 .. +31 of the LDS tile) against the
+// wave's kRC row chunks: 8 head-dim steps x (hi, lo).  Chunks without valid
+// rows hold zero Q fragments and are computed anyway (their results are
+// masked), which keeps the instruction stream branch-free.
+__device__ __forceinline__ void mma_chunk(const u16* bh, const u16* bl, int jc, int col, int half,
+                                          const bf16x8 (&qf)[kRC][8], f32x16* acc) {
+  const int r = jc * 32 + col;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int off = r * kHeadDim + swz16(8 * half + kk, r) * 8;
+    const bf16x8 vh = *reinterpret_cast<const bf16x8*>(bh + off);
+    const bf16x8 vl = *reinterpret_cast<const bf16x8*>(bl + off);
+#pragma unroll
+    for (int rc = 0; rc < kRC; ++rc)
+      acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], vh, kk ? acc[rc] : f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int rc = 0; rc < kRC; ++rc)
+      acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], vl, acc[rc], 0, 0, 0);
+  }
+}
+
+// Column max / exp-sum of one 32-key chunk over this wave's rows, merged over
+// the lane pair.  MASKED handles chunks with rows past the end of the block or
+// past the last head (rows of this lane: m = 8*(i/4) + 4*half + (i%4)); a
+// wave without any valid row yields (-inf, 0).
+template <bool MASKED>
+__device__ __forceinline__ float2 column_stats(const f32x16* acc, const float* csc,
+                                               const int* nval, int half) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int rc = 0; rc < kRC; ++rc) {
+    float mr = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      mr = fmaxf(mr, (!MASKED || row < nval[rc]) ? acc[rc][i] : -INFINITY);
+    }
+    m = fmaxf(m, mr * csc[rc]);  // scales are positive; -inf stays -inf
+  }
+  m = pair_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int rc = 0; rc < kRC; ++rc) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      const float e = __builtin_amdgcn_exp2f(fmaf(acc[rc][i], csc[rc], -m));
+      s += (!MASKED || row < nval[rc]) ? e : 0.f;
+    }
+  }
+  return make_float2(m, pair_sum(s));
+}
+
+// Issue order for one pipelined step (32 MFMAs, 16 LDS reads, the previous
+// chunk's max / exp / sum): each MFMA is followed by independent VALU work so
+// the in-order wave keeps issuing while the matrix core runs, and the ends the
+// region so the next step's accumulator reuse stays behind it.
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exp
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // other VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exp
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // other VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One LDS tile for this wave.  Full tiles (kJC chunks) run as one basic block
+// with two accumulator sets: chunk j+1's MFMAs overlap chunk j's statistics.
+template <bool MASKED>
+__device__ __forceinline__ void tile_chunks(const u16* bh, const u16* bl, int njc, int col,
+                                            int half, const bf16x8 (&qf)[kRC][8],
+                                            const float* csc, const int* nval, float2* part) {
+  f32x16 acc0[kRC], acc1[kRC];
+  if (njc == kJC) {
+    static_assert(kJC == 4, "pipeline below is written for 4 chunks per tile");
+    mma_chunk(bh, bl, 0, col, half, qf, acc0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_chunk(bh, bl, 1, col, half, qf, acc1);
+    const float2 s0 = column_stats<MASKED>(acc0, csc, nval, half);
+    interleave();
+    mma_chunk(bh, bl, 2, col, half, qf, acc0);
+    const float2 s1 = column_stats<MASKED>(acc1, csc, nval, half);
+    interleave();
+    mma_chunk(bh, bl, 3, col, half, qf, acc1);
+    const float2 s2 = column_stats<MASKED>(acc0, csc, nval, half);
+    interleave();
+    const float2 s3 = column_stats<MASKED>(acc1, csc, nval, half);
+    if (half == 0) {
+      part[col] = s0;
+      part[32 + col] = s1;
+      part[64 + col] = s2;
+      part[96 + col] = s3;
+    }
+  } else {
+    for (int jc = 0; jc < njc; ++jc) {
+      mma_chunk(bh, bl, jc, col, half, qf, acc0);
+      const float2 st = column_stats<MASKED>(acc0, csc, nval, half);
+      if (half == 0) part[jc * 32 + col] = st;
+    }
+  }
+}
+
+template <int QDT>
+__global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  ScoresSmem& sm = *reinterpret_cast<ScoresSmem*>(smem_raw);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -82,135 +214,94 @@ __global__ __launch_bounds__(512) void scores_kernel(
   const int col = lane & 31;
 
   // heaviest rows (largest I) first
-  const int64_t item = (int64_t)hkv * num_blocks - 1 - blockIdx.x;
-  const int h = (int)(item % hkv);
-  const int gb = (int)(item / hkv);
-  const int s = find_seq(boff, num_seqs, gb);
-  const int I = gb - boff[s];
-  const int len = cu[s + 1] - cu[s];
+  const int64_t item = (int64_t)a.hkv * a.num_blocks - 1 - blockIdx.x;
+  const int h = (int)(item % a.hkv);
+  const int gb = (int)(item / a.hkv);
+  const int s = find_seq(a.boff, a.num_seqs, gb);
+  const int I = gb - a.boff[s];
+  const int len = a.cu[s + 1] - a.cu[s];
   const int nI = min(kBlock, len - I * kBlock);
-  const int64_t tok0 = (int64_t)cu[s] + (int64_t)I * kBlock;
-  const u16* kbase = kmean16 + ((int64_t)h * num_blocks + boff[s]) * kHeadDim;
-  const int64_t lo_off = (int64_t)hkv * num_blocks * kHeadDim;  // lo part follows the hi part
-  float* out_row = scores + ((int64_t)h * num_blocks + gb) * max_blocks;
+  const int64_t tok0 = (int64_t)a.cu[s] + (int64_t)I * kBlock;
+  const u16* kbase = a.kmean16 + ((int64_t)h * a.num_blocks + a.boff[s]) * kHeadDim;
+  const int64_t lo_off = (int64_t)a.hkv * a.num_blocks * kHeadDim;  // lo part follows the hi part
+  float* out_row = a.scores + ((int64_t)h * a.num_blocks + gb) * a.max_blocks;
   const int ncols = I + 1;
-  const int ntiles = (ncols + kJTile - 1) / kJTile;
-  const int nchunks = 4 * group;  // 32-row chunks: (head, 32-token slice)
-  constexpr int kChunksPerPass = kWaves * RC;
+  const int ntiles = (ncols + kJT - 1) / kJT;
+  const int nchunks = 4 * a.group;  // 32-row chunks: (head, 32-token slice)
+
+  // Tile t of both terms = 64 segments of 1 KiB (4 key rows each); wave w
+  // issues segments 8w .. 8w+7.  Lane i of a segment copies physical chunk
+  // i%16 of key row 4*seg + i/16, i.e. logical chunk swz16(i%16, row).  Key
+  // rows past the causal range re-read the last valid row (results unused).
+  auto stage = [&](int tile, int buf) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int seg = wave * 8 + it;
+      const int term = seg >> 5;
+      const int sub = seg & 31;
+      const int r = 4 * sub + (lane >> 4);
+      const int J = min(tile * kJT + r, ncols - 1);
+      const u16* src = kbase + (term ? lo_off : 0) + (int64_t)J * kHeadDim + swz16(lane & 15, r) * 8;
+      load_lds16(src, &sm.kb[buf][term][sub * 512]);
+    }
+  };
 
   for (int pass = 0; pass * kChunksPerPass < nchunks; ++pass) {
-    // ---- Q fragments for this pass (read once) ----
-    bf16x8 qf[RC][8];
-    float cscale[RC];
-    int nvalid[RC];
+    // ---- Q fragments of this pass (read once) ----
+    bf16x8 qf[kRC][8];
+    float csc[kRC];
+    int nval[kRC];
+    bool masked = false;
 #pragma unroll
-    for (int rc = 0; rc < RC; ++rc) {
+    for (int rc = 0; rc < kRC; ++rc) {
       const int c = pass * kChunksPerPass + rc * kWaves + wave;
       const int hh = c >> 2;
       const int t0 = 32 * (c & 3);
       const bool head_ok = c < nchunks;
-      nvalid[rc] = head_ok ? max(0, min(32, nI - t0)) : 0;
-      const int hq_idx = h * group + (head_ok ? hh : 0);
-      const bool rvalid = col < nvalid[rc];
-      const int64_t row_elem = ((tok0 + t0 + col) * hq + hq_idx) * (int64_t)kHeadDim;
-      load_q_frag<QDT>(q, row_elem, rvalid, half, qf[rc]);
-      float sc = logit_scale * kLog2e;
-      if constexpr (QDT == FP_E4M3) sc *= q_scale[hq_idx];
-      cscale[rc] = sc;
+      nval[rc] = head_ok ? max(0, min(32, nI - t0)) : 0;
+      masked |= nval[rc] < 32;
+      const int hq_idx = h * a.group + (head_ok ? hh : 0);
+      const bool rvalid = col < nval[rc];
+      const int64_t row_elem = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim;
+      load_q_frag<QDT>(a.q, row_elem, rvalid, half, qf[rc]);
+      float sc = a.logit_scale * kLog2e;
+      if constexpr (QDT == FP_E4M3) sc *= a.q_scale[hq_idx];
+      csc[rc] = sc;
     }
 
-    // ---- stage pooled-key tile 0 (hi and lo parts) ----
-    auto stage_load = [&](int tile, uint4* regs) {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int c = it * 512 + (int)threadIdx.x;  // 16-byte chunk id in the tile
-        const int r = c >> 4, part16 = c & 15;
-        const int J = tile * kJTile + r;
-        const u16* src = kbase + (int64_t)J * kHeadDim + part16 * 8;
-        regs[it] = J < ncols ? *reinterpret_cast<const uint4*>(src) : uint4{0, 0, 0, 0};
-        regs[2 + it] = J < ncols ? *reinterpret_cast<const uint4*>(src + lo_off) : uint4{0, 0, 0, 0};
-      }
-    };
-    auto stage_store = [&](int buf, const uint4* regs) {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int c = it * 512 + (int)threadIdx.x;
-        const int r = c >> 4, part16 = c & 15;
-        *reinterpret_cast<uint4*>(&kb[buf][0][r * kKbStride + part16 * 8]) = regs[it];
-        *reinterpret_cast<uint4*>(&kb[buf][1][r * kKbStride + part16 * 8]) = regs[2 + it];
-      }
-    };
-    {
-      uint4 regs[4];
-      stage_load(0, regs);
-      stage_store(0, regs);
-    }
+    stage(0, 0);
+    wait_vm();
     __syncthreads();
 
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile & 1;
-      uint4 nxt[4];
-      const bool more = tile + 1 < ntiles;
-      if (more) stage_load(tile + 1, nxt);
+      if (tile + 1 < ntiles) stage(tile + 1, buf ^ 1);
+      const int njc = min(kJC, (ncols - tile * kJT + 31) >> 5);
+      const u16* bh = sm.kb[buf][0];
+      const u16* bl = sm.kb[buf][1];
+      if (masked)
+        tile_chunks<true>(bh, bl, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
+      else
+        tile_chunks<false>(bh, bl, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
 
-#pragma unroll
-      for (int jc = 0; jc < kJTile / 32; ++jc) {
-        const int boffs = (jc * 32 + col) * kKbStride + 64 * half;
-        float m_l = kNegBig;
-        f32x16 acc[RC];
-#pragma unroll
-        for (int rc = 0; rc < RC; ++rc) acc[rc] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&kb[buf][0][boffs + 8 * kk]);
-          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&kb[buf][1][boffs + 8 * kk]);
-#pragma unroll
-          for (int rc = 0; rc < RC; ++rc) {
-            acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], bh, acc[rc], 0, 0, 0);
-            acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], bl, acc[rc], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int rc = 0; rc < RC; ++rc) {
-          // rows of this lane: m = 8*(i/4) + 4*half + (i%4)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-            const float y = m < nvalid[rc] ? acc[rc][i] * cscale[rc] : -INFINITY;
-            acc[rc][i] = y;
-            m_l = fmaxf(m_l, y);
-          }
-        }
-        float s_l = 0.f;
-#pragma unroll
-        for (int rc = 0; rc < RC; ++rc)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s_l += __builtin_amdgcn_exp2f(acc[rc][i] - m_l);
-        const float m_p = __shfl_xor(m_l, 32, 64);
-        const float s_p = __shfl_xor(s_l, 32, 64);
-        const float m = fmaxf(m_l, m_p);
-        const float s = s_l * __builtin_amdgcn_exp2f(m_l - m) + s_p * __builtin_amdgcn_exp2f(m_p - m);
-        if (half == 0) part[buf][wave][jc * 32 + col] = make_float2(m, s);
-      }
-
-      if (more) stage_store(buf ^ 1, nxt);
+      wait_vm();
       __syncthreads();
 
-      if (threadIdx.x < kJTile) {
-        const int J = tile * kJTile + (int)threadIdx.x;
-        float m = kNegBig;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) m = fmaxf(m, part[buf][w][threadIdx.x].x);
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float2 p = part[buf][w][threadIdx.x];
-          s += p.y * __builtin_amdgcn_exp2f(p.x - m);
-        }
+      if (threadIdx.x < kJT) {
+        const int J = tile * kJT + (int)threadIdx.x;
         if (J < ncols) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm.part[buf][w][threadIdx.x].x);
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float2 p = sm.part[buf][w][threadIdx.x];
+            sum += p.y * __builtin_amdgcn_exp2f(p.x - m);  // inactive waves: (-inf, 0)
+          }
           // log2 domain -> natural log; passes after the first merge with the
           // value already stored
-          float L = (m + __log2f(s)) * kLn2;
+          float L = (m + __log2f(sum)) * kLn2;
           if (pass > 0) {
             const float P = out_row[J];
             const float hi = fmaxf(P, L);
@@ -224,29 +315,44 @@ __global__ __launch_bounds__(512) void scores_kernel(
   }
 }
 
+template <int QDT>
+hipError_t launch_scores_t(const ScoresArgs& a, dim3 grid, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)scores_kernel<QDT>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kScoresSmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((scores_kernel<QDT>), grid, dim3(64 * kWaves), kScoresSmem, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_scores(const Geometry& g, const int32_t* cu, const int32_t* boff, const void* q,
                          const float* q_scale, const u16* k_mean_bf16, float* scores,
                          hipStream_t st) {
   const dim3 grid((unsigned)(g.hkv * g.num_blocks));
-#define FP_SC(QD, RC)                                                                          \
-  hipLaunchKernelGGL((scores_kernel<QD, RC>), grid, dim3(512), 0, st, cu, boff, g.num_seqs,    \
-                     g.hq, g.hkv, g.group, g.num_blocks, g.max_blocks, g.softmax_scale, q,      \
-                     q_scale, k_mean_bf16, scores)
-#define FP_SC_RC(QD)                                  \
-  do {                                                \
-    if (g.group >= 8) FP_SC(QD, 4);                   \
-    else if (g.group >= 4) FP_SC(QD, 2);              \
-    else FP_SC(QD, 1);                                \
-  } while (0)
-  if (g.qk_dtype == FP_BF16) FP_SC_RC(FP_BF16);
-  else if (g.qk_dtype == FP_E4M3) FP_SC_RC(FP_E4M3);
-  else if (g.qk_dtype == FP_F32) FP_SC_RC(FP_F32);
-  else return hipErrorInvalidValue;
-#undef FP_SC_RC
-#undef FP_SC
-  return hipGetLastError();
+  ScoresArgs a;
+  a.cu = cu;
+  a.boff = boff;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.kmean16 = k_mean_bf16;
+  a.scores = scores;
+  a.num_blocks = g.num_blocks;
+  a.num_seqs = g.num_seqs;
+  a.hq = g.hq;
+  a.hkv = g.hkv;
+  a.group = g.group;
+  a.max_blocks = g.max_blocks;
+  a.logit_scale = g.softmax_scale;
+  if (g.qk_dtype == FP_BF16) return launch_scores_t<FP_BF16>(a, grid, st);
+  if (g.qk_dtype == FP_E4M3) return launch_scores_t<FP_E4M3>(a, grid, st);
+  if (g.qk_dtype == FP_F32) return launch_scores_t<FP_F32>(a, grid, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fp
