@@ -24,8 +24,11 @@ ARCH = "gfx950"
 
 SOURCES = ["fp_api.hip", "fp_pool.hip", "fp_scores.hip", "fp_select.hip", "fp_attn.hip"]
 
-# Packed fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are disabled for all device code.  IEEE mode is off
+# (max / min then need no NaN canonicalisation; no kernel relies on NaN
+# propagation: masked logits are -inf, never NaN).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mno-amdgpu-ieee", "-fno-honor-nans"]
 
 
 def hipcc() -> str:

@@ -46,6 +46,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // the bf16 / fp32 exponent range, and relative precision does not depend on
 // magnitude.  In practice the rescale then runs at most once per row.
 constexpr float kLazy = 64.0f;
+constexpr float kLazyBound = 18446744073709551616.0f;  // 2^kLazy
 constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
 #ifndef FP_ATTN_WAVES
 #define FP_ATTN_WAVES 8
@@ -96,6 +97,22 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const u16* p) {
 __device__ __forceinline__ void scale_acc(f32x16& x, float c) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] *= c;
+}
+
+// Issue order inside one pipeline block with NM MFMAs and ND LDS reads: each
+// MFMA is preceded by its share of the LDS reads and followed by independent
+// VALU work (the previous chunk's softmax), so the in-order wave keeps
+// issuing VALU while the matrix core runs.
+template <int NM, int ND>
+__device__ __forceinline__ void interleave() {
+  constexpr int kD = (ND + NM - 1) / NM;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kD, 0);  // LDS reads run two MFMAs ahead
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);  // DS read
+  }
 }
 
 __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
@@ -390,137 +407,181 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   auto iterate = [&](int t, auto pooled_c, auto diag_c) {
     constexpr bool POOLED_TILE = decltype(pooled_c)::value;
     const int buf = t & 1;
-    const bool pooled = POOLED_TILE;
-    const int idx = tile_index(t);
     if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
     const int page_next = fetch_page(t + 2);  // consumed after the math below
 
-    // The 128-key tile is processed as two 64-key halves (kh): QK^T, online
-    // softmax and PV per half keep the live score / probability registers at
-    // 64 + 32 per lane, while every K and V element is still read from LDS
-    // once per wave.
-    // One 64-key half of the tile, specialised (compile time) for kept,
-    // diagonal and pooled tiles so the softmax carries no per-element selects.
-    auto half_step = [&](int kh, auto pooled_c, auto diag_c) {
-      constexpr bool POOLED = decltype(pooled_c)::value;
-      constexpr bool DIAG = decltype(diag_c)::value;
-      // ---- S^T = K Q^T for keys 64 kh .. +63 ----
-      f32x16 sacc[RC][2];
-#pragma unroll
-      for (int rc = 0; rc < RC; ++rc)
-#pragma unroll
-        for (int k2c = 0; k2c < 2; ++k2c) sacc[rc][k2c] = f32x16{};
-      if constexpr (kFp8 && !POOLED) {
-        const uint8_t* kb = reinterpret_cast<const uint8_t*>(sm.k[buf]) + kh * 64 * 128;
-#pragma unroll
-        for (int k2c = 0; k2c < 2; ++k2c) {
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + koff8[2 * k2] + k2c * 32 * 128);
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + koff8[2 * k2 + 1] + k2c * 32 * 128);
-            const i32x8 av = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int rc = 0; rc < RC; ++rc)
-              sacc[rc][k2c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf8[rc][k2], sacc[rc][k2c], 0,
-                                                                              0, 0, 127, 0, 127);
-          }
-        }
-      } else {
-        const u16* kb = sm.k[buf] + kh * 64 * kHeadDim;
-#pragma unroll
-        for (int k2c = 0; k2c < 2; ++k2c) {
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + k2c * 32 * kHeadDim);
-#pragma unroll
-            for (int rc = 0; rc < RC; ++rc)
-              sacc[rc][k2c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[rc][kk], sacc[rc][k2c], 0, 0, 0);
-          }
-        }
-      }
+    // The 128-key tile runs as four 32-key chunks c in a software pipeline:
+    // block c issues the MFMAs of S(c+1) = K Q^T and O += V P(c-1) together
+    // with the online softmax of chunk c (VALU), which depends on neither, so
+    // one wave keeps the matrix core and the VALU busy at once.  The lazy-max
+    // rescale (rare) runs between blocks, after P(c-1) has been accumulated
+    // relative to the previous max.  Kept / diagonal / pooled variants are
+    // compile-time, so the softmax carries no per-element selects.
+    constexpr bool POOLED = POOLED_TILE;
+    constexpr bool DIAG = decltype(diag_c)::value;
+    constexpr bool kQk8 = kFp8 && !POOLED;
+    const u16* kt = sm.k[buf];
+    const u16* vt = sm.v[buf];
 
-      // ---- online softmax (log2 domain) ----
-      // lane's keys in this half: 64 kh + 32 k2c + 8 j + 4 half + e, slot i = 4 j + e
-      bf16x8 pb[RC][4];
-      float corr[RC];
-      bool need_rescale = false;
+    // S^T for keys 32 c .. +31: lane's query row col, keys 32 c + 8 (i/4) +
+    // 4 half + i%4 in slot i
+    auto qk = [&](int c, f32x16* sc) {
 #pragma unroll
-      for (int rc = 0; rc < RC; ++rc) {
-        if constexpr (POOLED) {
-          const float cs = c_pool;
+      for (int rc = 0; rc < RC; ++rc) sc[rc] = f32x16{};
+      if constexpr (kQk8) {
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(kt) + c * 32 * 128;
 #pragma unroll
-          for (int k2c = 0; k2c < 2; ++k2c)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float4 bv = *reinterpret_cast<const float4*>(&sm.bias[buf][64 * kh + 32 * k2c + 8 * j + 4 * half]);
-              sacc[rc][k2c][4 * j + 0] = fmaf(sacc[rc][k2c][4 * j + 0], cs, bv.x);
-              sacc[rc][k2c][4 * j + 1] = fmaf(sacc[rc][k2c][4 * j + 1], cs, bv.y);
-              sacc[rc][k2c][4 * j + 2] = fmaf(sacc[rc][k2c][4 * j + 2], cs, bv.z);
-              sacc[rc][k2c][4 * j + 3] = fmaf(sacc[rc][k2c][4 * j + 3], cs, bv.w);
-            }
-        }
-        if constexpr (DIAG) {
-          const int p_local = tbase + 32 * rc + col;
-#pragma unroll
-          for (int k2c = 0; k2c < 2; ++k2c)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = 64 * kh + 32 * k2c + 8 * (i >> 2) + 4 * half + (i & 3);
-              if (key > p_local) sacc[rc][k2c][i] = -INFINITY;
-            }
-        }
-        float mloc = sacc[rc][0][0];
-#pragma unroll
-        for (int k2c = 0; k2c < 2; ++k2c)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[rc][k2c][i]);
-        if constexpr (!POOLED) mloc *= c_kept;
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        // lazy max: keep the running max unless this half exceeds it by > kLazy
-        const float m_old = m_run[rc];
-        const float m_use = (mloc > m_old + kLazy) ? mloc : m_old;
-        need_rescale |= m_use != m_old;
-        corr[rc] = __builtin_amdgcn_exp2f(m_old - m_use);
-        m_run[rc] = m_use;
-        float lsum = 0.f;
-#pragma unroll
-        for (int k2c = 0; k2c < 2; ++k2c)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float arg;
-            if constexpr (POOLED) arg = sacc[rc][k2c][i] - m_use;
-            else arg = fmaf(sacc[rc][k2c][i], c_kept, -m_use);
-            const float pe = __builtin_amdgcn_exp2f(arg);
-            lsum += pe;
-            pb[rc][2 * k2c + (i >> 3)][i & 7] = f32_to_bf16(pe);
-          }
-        l_run[rc] = l_run[rc] * corr[rc] + lsum;
-      }
-      if (__any(need_rescale)) {
-#pragma unroll
-        for (int rc = 0; rc < RC; ++rc)
-#pragma unroll
-          for (int dc = 0; dc < 4; ++dc) scale_acc(o[rc][dc], corr[rc]);
-      }
-
-      // ---- O^T += V^T P^T over keys 64 kh .. +63 ----
-      const u16* vb = sm.v[buf] + kh * 64 * kHeadDim;
-#pragma unroll
-      for (int ksl = 0; ksl < 4; ++ksl) {
-#pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
-          const bf16x4 lo = lds_read_tr(vb + ksl * 16 * kHeadDim + voff[dc][0]);
-          const bf16x4 hi = lds_read_tr(vb + ksl * 16 * kHeadDim + voff[dc][1]);
-          const bf16x8 av = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + koff8[2 * k2]);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + koff8[2 * k2 + 1]);
+          const i32x8 av = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int rc = 0; rc < RC; ++rc)
-            o[rc][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rc][ksl], o[rc][dc], 0, 0, 0);
+            sc[rc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf8[rc][k2], sc[rc], 0, 0, 0, 127, 0, 127);
+        }
+      } else {
+        const u16* kb = kt + c * 32 * kHeadDim;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
+#pragma unroll
+          for (int rc = 0; rc < RC; ++rc)
+            sc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[rc][kk], sc[rc], 0, 0, 0);
         }
       }
     };
 
-#pragma unroll 1
-    for (int kh = 0; kh < 2; ++kh) half_step(kh, pooled_c, diag_c);
+    // O^T += V^T P^T over keys 32 c .. +31 (two 16-key MFMA steps)
+    auto pv = [&](int c, const bf16x8 (*pp)[2]) {
+      const u16* vb = vt + c * 32 * kHeadDim;
+#pragma unroll
+      for (int s16 = 0; s16 < 2; ++s16) {
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) {
+          const bf16x4 lo = lds_read_tr(vb + s16 * 16 * kHeadDim + voff[dc][0]);
+          const bf16x4 hi = lds_read_tr(vb + s16 * 16 * kHeadDim + voff[dc][1]);
+          const bf16x8 av = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int rc = 0; rc < RC; ++rc)
+            o[rc][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pp[rc][s16], o[rc][dc], 0, 0, 0);
+        }
+      }
+    };
+
+    // Online softmax of chunk c (log2 domain) -> bf16 probabilities in the
+    // P^T operand layout and the chunk's row sums.  Fast path: exponentiate
+    // against the running max m_run as is.  The max only has to move when a
+    // logit exceeds m_run + kLazy, and then that row's chunk sum exceeds
+    // 2^kLazy (a row's first chunk, with m_run = -inf, gives +inf), so the sum
+    // doubles as the overflow test and the fast path computes no max at all.
+    // The slow path (rare) raises the max of the affected rows, rescales the
+    // output and recomputes the chunk.
+    auto finish_logits = [&](int c, f32x16* sc) {
+#pragma unroll
+      for (int rc = 0; rc < RC; ++rc) {
+        if constexpr (POOLED) {
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const float4 bv = *reinterpret_cast<const float4*>(&sm.bias[buf][32 * c + 8 * jq + 4 * half]);
+            sc[rc][4 * jq + 0] = fmaf(sc[rc][4 * jq + 0], c_pool, bv.x);
+            sc[rc][4 * jq + 1] = fmaf(sc[rc][4 * jq + 1], c_pool, bv.y);
+            sc[rc][4 * jq + 2] = fmaf(sc[rc][4 * jq + 2], c_pool, bv.z);
+            sc[rc][4 * jq + 3] = fmaf(sc[rc][4 * jq + 3], c_pool, bv.w);
+          }
+        }
+        if constexpr (DIAG) {
+          const int p_local = tbase + 32 * rc + col;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = 32 * c + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (key > p_local) sc[rc][i] = -INFINITY;
+          }
+        }
+      }
+    };
+    auto exponentiate = [&](const f32x16* sc, bf16x8 (*pp)[2], float* ls) {
+#pragma unroll
+      for (int rc = 0; rc < RC; ++rc) {
+        const float m = m_run[rc];
+        float lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float arg;
+          if constexpr (POOLED) arg = sc[rc][i] - m;
+          else arg = fmaf(sc[rc][i], c_kept, -m);
+          const float pe = __builtin_amdgcn_exp2f(arg);
+          lsum += pe;
+          pp[rc][i >> 3][i & 7] = f32_to_bf16(pe);
+        }
+        ls[rc] = lsum;
+      }
+    };
+    auto softmax = [&](int c, f32x16* sc, bf16x8 (*pp)[2], float* ls) -> bool {
+      finish_logits(c, sc);
+      exponentiate(sc, pp, ls);
+      bool over = false;
+#pragma unroll
+      for (int rc = 0; rc < RC; ++rc) over |= !(ls[rc] <= kLazyBound);
+      return over;
+    };
+    // The probabilities and row sums of the block are pinned before the
+    // branch so that they stay inside the pipeline block (otherwise they are
+    // sunk past it, next to their first use).
+    auto settle = [&](bool over, f32x16* sc, bf16x8 (*pp)[2], float* ls) {
+#pragma unroll
+      for (int rc = 0; rc < RC; ++rc) asm volatile("" ::"v"(pp[rc][0]), "v"(pp[rc][1]), "v"(ls[rc]));
+      if (__any(over)) {
+        float corr[RC];
+#pragma unroll
+        for (int rc = 0; rc < RC; ++rc) {
+          float mloc = sc[rc][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, sc[rc][i]);
+          if constexpr (!POOLED) mloc *= c_kept;
+          mloc = pair_max(mloc);
+          const float m_old = m_run[rc];
+          const float m_use = (mloc > m_old + kLazy) ? mloc : m_old;
+          corr[rc] = __builtin_amdgcn_exp2f(m_old - m_use);
+          m_run[rc] = m_use;
+          l_run[rc] *= corr[rc];
+        }
+#pragma unroll
+        for (int rc = 0; rc < RC; ++rc)
+#pragma unroll
+          for (int dc = 0; dc < 4; ++dc) scale_acc(o[rc][dc], corr[rc]);
+        exponentiate(sc, pp, ls);
+      }
+#pragma unroll
+      for (int rc = 0; rc < RC; ++rc) l_run[rc] += ls[rc];
+    };
+
+    constexpr int kQkM = (kQk8 ? 2 : 8) * RC;  // MFMAs of one qk(c)
+    constexpr int kQkD = kQk8 ? 4 : 8;         // LDS reads of one qk(c)
+    constexpr int kPvM = 8 * RC, kPvD = 16;
+    f32x16 sa[RC], sb[RC];
+    bf16x8 pa[RC][2], pq[RC][2];
+    float la[RC], lq[RC];
+    qk(0, sa);
+    __builtin_amdgcn_sched_barrier(0);
+    qk(1, sb);
+    bool ov = softmax(0, sa, pa, la);
+    interleave<kQkM, kQkD>();
+    settle(ov, sa, pa, la);
+    qk(2, sa);
+    pv(0, pa);
+    ov = softmax(1, sb, pq, lq);
+    interleave<kQkM + kPvM, kQkD + kPvD>();
+    settle(ov, sb, pq, lq);
+    qk(3, sb);
+    pv(1, pq);
+    ov = softmax(2, sa, pa, la);
+    interleave<kQkM + kPvM, kQkD + kPvD>();
+    settle(ov, sa, pa, la);
+    pv(2, pa);
+    ov = softmax(3, sb, pq, lq);
+    interleave<kPvM, kPvD>();
+    settle(ov, sb, pq, lq);
+    pv(3, pq);
 
     publish_slot(t + 2, page_next, buf);
     wait_vm();
