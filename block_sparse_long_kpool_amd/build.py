@@ -24,11 +24,12 @@ ARCH = "gfx950"
 
 SOURCES = ["fp_api.hip", "fp_pool.hip", "fp_scores.hip", "fp_select.hip", "fp_attn.hip"]
 
-# Packed fp32 VALU forms are disabled for all device code.  IEEE mode is off
-# (max / min then need no NaN canonicalisation; no kernel relies on NaN
-# propagation: masked logits are -inf, never NaN).
+# Packed fp32 VALU forms are disabled for all device code.  Device code runs
+# with IEEE mode off (max / min then need no NaN canonicalisation; no kernel
+# relies on NaN propagation: masked logits are -inf, never NaN).  Host code
+# keeps full NaN semantics (argument validation tests for NaN).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mno-amdgpu-ieee", "-fno-honor-nans"]
+                "-Xarch_device", "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans"]
 
 
 def hipcc() -> str:
