@@ -30,19 +30,14 @@ namespace {
 constexpr float kGuard = 2e-3f;
 constexpr int kRowsPerWg = 4;
 
-template <int QDT>
-__device__ __forceinline__ double q_elem(const void* q, int64_t e) {
-  if constexpr (QDT == FP_BF16) {
-    return (double)bf16_bits_to_f32(reinterpret_cast<const u16*>(q)[e]);
-  } else if constexpr (QDT == FP_E4M3) {
-    return (double)e4m3_to_f32(reinterpret_cast<const uint8_t*>(q)[e]);
-  } else {
-    return (double)(float)f32_to_bf16(reinterpret_cast<const float*>(q)[e]);
-  }
-}
+// Exact score of pooled key J for the rows of (h, block I):
+// ln sum_r exp(x_rJ - ref) + ref, all in float64 (q as stored, widened; fp32
+// q rounded to bf16 first, as everywhere on this path).  One wave; lane l
+// takes rows l, l + 64, ... and reads each row with 16-byte loads into four
+// independent accumulators.  kbar is wave-uniform.
+__device__ __forceinline__ double bf16_lo(unsigned w) { return (double)__uint_as_float(w << 16); }
+__device__ __forceinline__ double bf16_hi(unsigned w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
 
-// Exact log2-free score of pooled key J for the rows of (h, block I):
-// ln sum_r exp(x_rJ - ref) + ref, all in float64.  One wave.
 template <int QDT>
 __device__ double exact_score(const void* q, const float* q_scale, const float* kbar, int hq,
                               int group, int h, int64_t tok0, int nI, double scale, double ref,
@@ -54,9 +49,46 @@ __device__ double exact_score(const void* q, const float* q_scale, const float* 
     const int t = r - hh * nI;
     const int hq_idx = h * group + hh;
     const int64_t e0 = ((tok0 + t) * hq + hq_idx) * (int64_t)kHeadDim;
-    double dot = 0.0;
-    for (int d = 0; d < kHeadDim; ++d) dot = fma(q_elem<QDT>(q, e0 + d), (double)kbar[d], dot);
-    double x = scale * dot;
+    double d[4] = {0.0, 0.0, 0.0, 0.0};
+    if constexpr (QDT == FP_BF16) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(q) + e0);
+#pragma unroll 4
+      for (int c = 0; c < 16; ++c) {
+        const uint4 w = p[c];
+        const float* kb = kbar + 8 * c;
+        d[0] = fma(bf16_lo(w.x), (double)kb[0], d[0]);
+        d[1] = fma(bf16_hi(w.x), (double)kb[1], d[1]);
+        d[2] = fma(bf16_lo(w.y), (double)kb[2], d[2]);
+        d[3] = fma(bf16_hi(w.y), (double)kb[3], d[3]);
+        d[0] = fma(bf16_lo(w.z), (double)kb[4], d[0]);
+        d[1] = fma(bf16_hi(w.z), (double)kb[5], d[1]);
+        d[2] = fma(bf16_lo(w.w), (double)kb[6], d[2]);
+        d[3] = fma(bf16_hi(w.w), (double)kb[7], d[3]);
+      }
+    } else if constexpr (QDT == FP_E4M3) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(q) + e0);
+#pragma unroll 2
+      for (int c = 0; c < 8; ++c) {
+        const uint4 w = p[c];
+        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+        const float* kb = kbar + 16 * c;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          d[e & 3] = fma((double)e4m3_to_f32((ws[e >> 2] >> (8 * (e & 3))) & 0xFFu), (double)kb[e], d[e & 3]);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e0);
+#pragma unroll 4
+      for (int c = 0; c < 32; ++c) {
+        const float4 v = p[c];
+        const float* kb = kbar + 4 * c;
+        d[0] = fma((double)(float)f32_to_bf16(v.x), (double)kb[0], d[0]);
+        d[1] = fma((double)(float)f32_to_bf16(v.y), (double)kb[1], d[1]);
+        d[2] = fma((double)(float)f32_to_bf16(v.z), (double)kb[2], d[2]);
+        d[3] = fma((double)(float)f32_to_bf16(v.w), (double)kb[3], d[3]);
+      }
+    }
+    double x = scale * ((d[0] + d[1]) + (d[2] + d[3]));
     if constexpr (QDT == FP_E4M3) x *= (double)q_scale[hq_idx];
     acc += exp(x - ref);
   }
