@@ -83,7 +83,8 @@ struct SharedMem {
   float bias[2][kBlock];
   int slot[2][kBlock];  // cache slot (page * page_size + offset) of each token row of a kept tile
   uint32_t kept_bits[kMaxBlocksPerSeq / 32];
-  int pooled_list[kMaxBlocksPerSeq / kBlock];
+  // tile list of the row: kept blocks (list order), then pooled tile indices
+  uint16_t tiles[kMaxBlocksPerSeq + kMaxBlocksPerSeq / kBlock];
   int npooled;
 };
 
@@ -97,22 +98,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const u16* p) {
 __device__ __forceinline__ void scale_acc(f32x16& x, float c) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] *= c;
-}
-
-// Issue order inside one pipeline block with NM MFMAs and ND LDS reads: each
-// MFMA is preceded by its share of the LDS reads and followed by independent
-// VALU work (the previous chunk's softmax), so the in-order wave keeps
-// issuing VALU while the matrix core runs.
-template <int NM, int ND>
-__device__ __forceinline__ void interleave() {
-  constexpr int kD = (ND + NM - 1) / NM;
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kD, 0);  // LDS reads run two MFMAs ahead
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
-    __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);  // DS read
-  }
 }
 
 __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
@@ -154,7 +139,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int64_t tok0 = (int64_t)a.cu[s] + (int64_t)I * kBlock;
   const int64_t pooled_base = (int64_t)h * a.num_blocks + a.boff[s];
   const int kbeg = a.row_ptr[row];
-  const int nkept = a.row_ptr[row + 1] - kbeg;
+  // a valid list holds at most I + 1 blocks (the LDS tile list is sized for it)
+  const int nkept = min(max(a.row_ptr[row + 1] - kbeg, 0), I + 1);
   const int64_t ptrow = (int64_t)s * a.max_pages;
 
   const int hh = 2 * pack + (wave * RC) / 4;
@@ -162,14 +148,20 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int hq_idx = h * a.group + (head_ok ? hh : 0);
   const int tbase = 32 * ((wave * RC) % 4);
 
-  // ---- kept-block bitmap and the pooled tiles that hold a pruned block ----
+  // ---- tile list in LDS, kept-block bitmap, pooled tiles ----
+  // The row's list is copied once so that every per-tile lookup is an LDS
+  // read.  Entries are clamped to [0, I] for addressing (a list from the
+  // selection stage is always in range; out-of-range entries from other
+  // producers give unspecified output but no out-of-bounds access).
   const int nwords = (I >> 5) + 1;
-  if (a.correction) {
+  if (a.correction)
     for (int w = tid; w < nwords; w += NT) sm.kept_bits[w] = 0u;
-    __syncthreads();
+  for (int i = tid; i < nkept; i += NT) sm.tiles[i] = (uint16_t)min(max(a.col_idx[kbeg + i], 0), I);
+  __syncthreads();
+  if (a.correction) {
     for (int i = tid; i < nkept; i += NT) {
-      const int J = a.col_idx[kbeg + i];
-      if ((unsigned)J <= (unsigned)I) atomicOr(&sm.kept_bits[J >> 5], 1u << (J & 31));
+      const int J = sm.tiles[i];
+      atomicOr(&sm.kept_bits[J >> 5], 1u << (J & 31));
     }
     __syncthreads();
     if (wave == 0) {
@@ -189,7 +181,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
           }
         }
         const unsigned long long mb = __ballot(any_pruned);
-        if (any_pruned) sm.pooled_list[cnt + __popcll(mb & ((1ull << lane) - 1ull))] = pt;
+        if (any_pruned) sm.tiles[nkept + cnt + __popcll(mb & ((1ull << lane) - 1ull))] = (uint16_t)pt;
         cnt += __popcll(mb);
       }
       if (lane == 0) sm.npooled = cnt;
@@ -213,18 +205,18 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int psz = a.page_size;
   const bool small_pages = psz <= kBlock;
   const int pshift = 31 - __clz(psz);
-  auto tile_index = [&](int t) { return t >= nkept ? sm.pooled_list[t - nkept] : a.col_idx[kbeg + t]; };
+  auto tile_index = [&](int t) { return (int)sm.tiles[t]; };
   // page id of row `tid` of kept tile t (only threads < 128); -1 if pooled
   auto fetch_page = [&](int t) -> int {
     if (t >= ntiles || t >= nkept || tid >= kBlock) return -1;
-    const int J = a.col_idx[kbeg + t];
+    const int J = tile_index(t);
     const int p0 = J * kBlock + tid;
     const int p = p0 < len ? p0 : J * kBlock;
     return a.page_table[ptrow + (small_pages ? (p >> pshift) : (p / psz))];
   };
   auto publish_slot = [&](int t, int page, int sbuf) {
     if (t >= ntiles || t >= nkept || tid >= kBlock) return;
-    const int J = a.col_idx[kbeg + t];
+    const int J = tile_index(t);
     const int p0 = J * kBlock + tid;
     const int p = p0 < len ? p0 : J * kBlock;
     sm.slot[sbuf][tid] = page * psz + (small_pages ? (p & (psz - 1)) : (p % psz));

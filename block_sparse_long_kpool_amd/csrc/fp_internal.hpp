@@ -116,6 +116,22 @@ __device__ __forceinline__ float pair_max(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Issue order inside one pipeline block with NM MFMAs and ND LDS reads: each
+// MFMA is preceded by its share of the LDS reads and followed by independent
+// VALU work (the previous chunk's softmax), so the in-order wave keeps
+// issuing VALU while the matrix core runs.
+template <int NM, int ND>
+__device__ __forceinline__ void interleave() {
+  constexpr int kD = (ND + NM - 1) / NM;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kD, 0);  // LDS reads run two MFMAs ahead
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);  // DS read
+  }
+}
+
 // ---- launchers (one per translation unit) ---------------------------------
 
 // Block offsets boff[num_seqs + 1] from cu_seqlens (prefix of ceil(len/128)).

@@ -149,24 +149,6 @@ __device__ __forceinline__ float2 column_stats(const f32x16* acc, const float* c
   return make_float2(m, pair_sum(s));
 }
 
-// Issue order for one pipelined step (32 MFMAs, 16 LDS reads, the previous
-// chunk's max / exp / sum): each MFMA is followed by independent VALU work so
-// the in-order wave keeps issuing while the matrix core runs, and the ends the
-// region so the next step's accumulator reuse stays behind it.
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exp
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // other VALU
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // exp
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // other VALU
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // One LDS tile for this wave.  Full tiles (kJC chunks) run as one basic block
 // with two accumulator sets: chunk j+1's MFMAs overlap chunk j's statistics.
 template <bool MASKED>
@@ -180,13 +162,13 @@ __device__ __forceinline__ void tile_chunks(const u16* bh, const u16* bl, int nj
     __builtin_amdgcn_sched_barrier(0);
     mma_chunk(bh, bl, 1, col, half, qf, acc1);
     const float2 s0 = column_stats<MASKED>(acc0, csc, nval, half);
-    interleave();
+    interleave<16 * kRC, 16>();
     mma_chunk(bh, bl, 2, col, half, qf, acc0);
     const float2 s1 = column_stats<MASKED>(acc1, csc, nval, half);
-    interleave();
+    interleave<16 * kRC, 16>();
     mma_chunk(bh, bl, 3, col, half, qf, acc1);
     const float2 s2 = column_stats<MASKED>(acc0, csc, nval, half);
-    interleave();
+    interleave<16 * kRC, 16>();
     const float2 s3 = column_stats<MASKED>(acc1, csc, nval, half);
     if (half == 0) {
       part[col] = s0;
