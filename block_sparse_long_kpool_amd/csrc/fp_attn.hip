@@ -81,7 +81,9 @@ struct SharedMem {
   u16 k[2][kTileElems];  // fp8 tiles use the first half of a buffer
   u16 v[2][kTileElems];
   float bias[2][kBlock];
-  int slot[2][kBlock];  // cache slot (page * page_size + offset) of each token row of a kept tile
+  // element offset ((page * page_size + offset) * Hkv + h) * d of each token
+  // row of a kept tile in the paged K/V caches
+  int64_t slot[2][kBlock];
   uint32_t kept_bits[kMaxBlocksPerSeq / 32];
   // tile list of the row: kept blocks (list order), then pooled tile indices
   uint16_t tiles[kMaxBlocksPerSeq + kMaxBlocksPerSeq / kBlock];
@@ -219,7 +221,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     const int J = tile_index(t);
     const int p0 = J * kBlock + tid;
     const int p = p0 < len ? p0 : J * kBlock;
-    sm.slot[sbuf][tid] = page * psz + (small_pages ? (p & (psz - 1)) : (p % psz));
+    const int cslot = page * psz + (small_pages ? (p & (psz - 1)) : (p % psz));
+    sm.slot[sbuf][tid] = ((int64_t)cslot * a.hkv + h) * kHeadDim;
   };
   auto issue_tile = [&](int t, int buf) {
     const bool pooled = t >= nkept;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       const int nJ = min(kBlock, len - J * kBlock);
       sm.bias[buf][tid] = (J <= I && !kept) ? __log2f((float)nJ) : -INFINITY;
     }
-    const int* slots = sm.slot[buf];
+    const int64_t* slots = sm.slot[buf];
     if constexpr (kF32) {
       // fp32 cache: load, round to bf16, store swizzled (no async path)
       for (int it = 0; it < 2048 / NT; ++it) {
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
           kw = *reinterpret_cast<const uint4*>(a.km16 + (pooled_base + J) * kHeadDim + c * 8);
           vw = *reinterpret_cast<const uint4*>(a.vm16 + (pooled_base + J) * kHeadDim + c * 8);
         } else {
-          const int64_t e = ((int64_t)slots[r] * a.hkv + h) * kHeadDim + c * 8;
+          const int64_t e = slots[r] + c * 8;
           const float* ks = reinterpret_cast<const float*>(a.k_cache) + e;
           const float* vs = reinterpret_cast<const float*>(a.v_cache) + e;
           const uint2 ka = f32x4_to_bf16x4(*reinterpret_cast<const float4*>(ks));
@@ -274,28 +277,32 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       return;
     }
     const u16* vc = reinterpret_cast<const u16*>(a.v_cache);
+    // all row offsets first (one LDS wait), then the gathers
+    int64_t rowoff[32 / NW];
+#pragma unroll
+    for (int it = 0; it < 32 / NW; ++it) rowoff[it] = slots[(wave * (32 / NW) + it) * 4 + sub];
 #pragma unroll
     for (int it = 0; it < 32 / NW; ++it) {
       const int wi = wave * (32 / NW) + it;
       const int r = wi * 4 + sub;
-      const int c = swz16(pc, r);
-      const int64_t tokrow = ((int64_t)slots[r] * a.hkv + h) * kHeadDim;
-      load_lds16(vc + tokrow + c * 8, &sm.v[buf][wi * 512]);
+      const int64_t e = rowoff[it] + swz16(pc, r) * 8;
+      load_lds16(vc + e, &sm.v[buf][wi * 512]);
       if constexpr (!kFp8) {
-        load_lds16(reinterpret_cast<const u16*>(a.k_cache) + tokrow + c * 8, &sm.k[buf][wi * 512]);
+        load_lds16(reinterpret_cast<const u16*>(a.k_cache) + e, &sm.k[buf][wi * 512]);
       }
     }
     if constexpr (kFp8) {
       // fp8 rows of 128 B: each wave-instruction fills 8 rows
       const int sub8 = lane >> 3, pc8 = lane & 7;
       uint8_t* kb = reinterpret_cast<uint8_t*>(sm.k[buf]);
+      int64_t rowoff8[16 / NW];
+#pragma unroll
+      for (int it = 0; it < 16 / NW; ++it) rowoff8[it] = slots[(wave * (16 / NW) + it) * 8 + sub8];
 #pragma unroll
       for (int it = 0; it < 16 / NW; ++it) {
         const int wi = wave * (16 / NW) + it;
         const int r = wi * 8 + sub8;
-        const int c = swz8(pc8, r);
-        const int64_t tokrow = ((int64_t)slots[r] * a.hkv + h) * kHeadDim;
-        load_lds16(reinterpret_cast<const uint8_t*>(a.k_cache) + tokrow + c * 16, kb + wi * 1024);
+        load_lds16(reinterpret_cast<const uint8_t*>(a.k_cache) + rowoff8[it] + swz8(pc8, r) * 16, kb + wi * 1024);
       }
     }
   };
