@@ -150,6 +150,50 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int hq_idx = h * a.group + (head_ok ? hh : 0);
   const int tbase = 32 * ((wave * RC) % 4);
 
+  // ---- Q^T fragments (B operand), kept for the whole kernel ----
+  // (issued first: their latency overlaps the list set-up below)
+  // lane owns row col of chunk rc; head-dim slots 64*half + 8*kk + i
+  bf16x8 qf[RC][8];
+  i32x8 qf8[RC][2];
+  int nvalid[RC];
+#pragma unroll
+  for (int rc = 0; rc < RC; ++rc) {
+    const int t0 = tbase + 32 * rc;
+    nvalid[rc] = head_ok ? max(0, min(32, nI - t0)) : 0;
+    const bool rvalid = col < nvalid[rc];
+    const int64_t e0 = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim + 64 * half;
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        i32x8 v = i32x8{};
+        if (rvalid) {
+          const i32x4* p = reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(a.q) + e0 + 32 * k2);
+          const i32x4 lo = p[0], hi = p[1];
+          v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        qf8[rc][k2] = v;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) qf[rc][kk] = bf16x8{};
+    } else if constexpr (QDT == FP_BF16) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        qf[rc][kk] = rvalid ? *reinterpret_cast<const bf16x8*>(reinterpret_cast<const u16*>(a.q) + e0 + 8 * kk)
+                            : bf16x8{};
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        if (rvalid) {
+          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + e0 + 8 * kk);
+          const float4 x = p[0], y = p[1];
+          qf[rc][kk] = bf16x8{f32_to_bf16(x.x), f32_to_bf16(x.y), f32_to_bf16(x.z), f32_to_bf16(x.w),
+                              f32_to_bf16(y.x), f32_to_bf16(y.y), f32_to_bf16(y.z), f32_to_bf16(y.w)};
+        } else {
+          qf[rc][kk] = bf16x8{};
+        }
+      }
+    }
+  }
   // ---- tile list in LDS, kept-block bitmap, pooled tiles ----
   // The row's list is copied once so that every per-tile lookup is an LDS
   // read.  Entries are clamped to [0, I] for addressing (a list from the
@@ -307,49 +351,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     }
   };
 
-  // ---- Q^T fragments (B operand), kept for the whole kernel ----
-  // lane owns row col of chunk rc; head-dim slots 64*half + 8*kk + i
-  bf16x8 qf[RC][8];
-  i32x8 qf8[RC][2];
-  int nvalid[RC];
-#pragma unroll
-  for (int rc = 0; rc < RC; ++rc) {
-    const int t0 = tbase + 32 * rc;
-    nvalid[rc] = head_ok ? max(0, min(32, nI - t0)) : 0;
-    const bool rvalid = col < nvalid[rc];
-    const int64_t e0 = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim + 64 * half;
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        i32x8 v = i32x8{};
-        if (rvalid) {
-          const i32x4* p = reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(a.q) + e0 + 32 * k2);
-          const i32x4 lo = p[0], hi = p[1];
-          v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        qf8[rc][k2] = v;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qf[rc][kk] = bf16x8{};
-    } else if constexpr (QDT == FP_BF16) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        qf[rc][kk] = rvalid ? *reinterpret_cast<const bf16x8*>(reinterpret_cast<const u16*>(a.q) + e0 + 8 * kk)
-                            : bf16x8{};
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        if (rvalid) {
-          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + e0 + 8 * kk);
-          const float4 x = p[0], y = p[1];
-          qf[rc][kk] = bf16x8{f32_to_bf16(x.x), f32_to_bf16(x.y), f32_to_bf16(x.z), f32_to_bf16(x.w),
-                              f32_to_bf16(y.x), f32_to_bf16(y.y), f32_to_bf16(y.z), f32_to_bf16(y.w)};
-        } else {
-          qf[rc][kk] = bf16x8{};
-        }
-      }
-    }
-  }
   // log2-domain logit scales: kept tiles and pooled tiles
   float c_kept = a.softmax_scale * kLog2e;
   float c_pool = c_kept;
@@ -371,10 +372,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   }
 
   // prologue: slots of tiles 0 and 1, gathers of tile 0
-  publish_slot(0, fetch_page(0), 0);
+  {
+    const int page0 = fetch_page(0);  // both page lookups in flight together
+    const int page1 = fetch_page(1);
+    publish_slot(0, page0, 0);
+    publish_slot(1, page1, 1);
+  }
   __syncthreads();
   if (ntiles > 0) issue_tile(0, 0);
-  publish_slot(1, fetch_page(1), 1);
   wait_vm();
   __syncthreads();
 
