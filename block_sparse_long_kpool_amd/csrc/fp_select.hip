@@ -96,16 +96,98 @@ __device__ double exact_score(const void* q, const float* q_scale, const float* 
   return log(acc) + ref;
 }
 
+// The same exact score computed by a whole workgroup of kSelThreads threads
+// (rows split across all of them, one block-wide reduction).  Called
+// uniformly by every thread.
+constexpr int kSelThreads = 256;
+
 template <int QDT>
-__global__ __launch_bounds__(256) void decide_kernel(
+__device__ double exact_score_wg(const void* q, const float* q_scale, const float* kbar, int hq,
+                                 int group, int h, int64_t tok0, int nI, double scale, double ref,
+                                 double* red) {
+  const int R = group * nI;
+  double acc = 0.0;
+  for (int r = threadIdx.x; r < R; r += kSelThreads) {
+    const int hh = r / nI;
+    const int t = r - hh * nI;
+    const int hq_idx = h * group + hh;
+    const int64_t e0 = ((tok0 + t) * hq + hq_idx) * (int64_t)kHeadDim;
+    double d[4] = {0.0, 0.0, 0.0, 0.0};
+    if constexpr (QDT == FP_BF16) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(q) + e0);
+#pragma unroll 4
+      for (int c = 0; c < 16; ++c) {
+        const uint4 w = p[c];
+        const float* kb = kbar + 8 * c;
+        d[0] = fma(bf16_lo(w.x), (double)kb[0], d[0]);
+        d[1] = fma(bf16_hi(w.x), (double)kb[1], d[1]);
+        d[2] = fma(bf16_lo(w.y), (double)kb[2], d[2]);
+        d[3] = fma(bf16_hi(w.y), (double)kb[3], d[3]);
+        d[0] = fma(bf16_lo(w.z), (double)kb[4], d[0]);
+        d[1] = fma(bf16_hi(w.z), (double)kb[5], d[1]);
+        d[2] = fma(bf16_lo(w.w), (double)kb[6], d[2]);
+        d[3] = fma(bf16_hi(w.w), (double)kb[7], d[3]);
+      }
+    } else if constexpr (QDT == FP_E4M3) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(q) + e0);
+#pragma unroll 2
+      for (int c = 0; c < 8; ++c) {
+        const uint4 w = p[c];
+        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+        const float* kb = kbar + 16 * c;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          d[e & 3] = fma((double)e4m3_to_f32((ws[e >> 2] >> (8 * (e & 3))) & 0xFFu), (double)kb[e], d[e & 3]);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e0);
+#pragma unroll 4
+      for (int c = 0; c < 32; ++c) {
+        const float4 v = p[c];
+        const float* kb = kbar + 4 * c;
+        d[0] = fma((double)(float)f32_to_bf16(v.x), (double)kb[0], d[0]);
+        d[1] = fma((double)(float)f32_to_bf16(v.y), (double)kb[1], d[1]);
+        d[2] = fma((double)(float)f32_to_bf16(v.z), (double)kb[2], d[2]);
+        d[3] = fma((double)(float)f32_to_bf16(v.w), (double)kb[3], d[3]);
+      }
+    }
+    double x = scale * ((d[0] + d[1]) + (d[2] + d[3]));
+    if constexpr (QDT == FP_E4M3) x *= (double)q_scale[hq_idx];
+    acc += exp(x - ref);
+  }
+  acc = wave_sum_d(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) tot += red[w];
+  __syncthreads();  // red is reused by the next call
+  return log(tot) + ref;
+}
+
+// One workgroup per CSR row.  Pass 1 (threads over J, wave ballots): the fast
+// keep bits and two candidate bitmaps in LDS, one for entries within kGuard of
+// the threshold (never forced blocks) and one for entries within kGuard of the
+// row max.  Pass 2, only if a threshold candidate exists: the exact row max
+// over the max candidates, then the exact decision of every threshold
+// candidate, each evaluated by the whole workgroup.  Pass 3 writes every word
+// of the row's bitmask and the count.
+template <int QDT>
+__global__ __launch_bounds__(kSelThreads) void decide_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ boff, int num_seqs, int hq,
     int hkv, int group, int64_t num_blocks, int max_blocks, float softmax_scale,
     const void* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ k_mean, const float* __restrict__ scores, float alpha, int n_sink,
     int n_local, uint32_t* __restrict__ keep_bits, int32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + (threadIdx.x >> 6);
-  if (row >= (int64_t)hkv * num_blocks) return;
+  constexpr int kW = kMaxBlocksPerSeq / 32;
+  __shared__ uint32_t keep_fast[kW + 1], cand_thr[kW + 1], cand_max[kW + 1], keep_fix[kW + 1];
+  __shared__ float redf[kSelThreads / 64];
+  __shared__ int redi[kSelThreads / 64];
+  __shared__ double redd[kSelThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row = blockIdx.x;
   const int h = (int)(row / num_blocks);
   const int gb = (int)(row % num_blocks);
   const int s = find_seq(boff, num_seqs, gb);
@@ -114,32 +196,60 @@ __global__ __launch_bounds__(256) void decide_kernel(
   uint32_t* bits = keep_bits + row * words;
   const float* L = scores + row * max_blocks;
   const int ncols = I + 1;
+  const int nw_row = (ncols + 31) >> 5;
 
   if (!(alpha > 0.f)) {  // alpha <= 0 (or NaN): every causal block
-    for (int w = lane; w < words; w += 64) {
+    for (int w = tid; w < words; w += kSelThreads) {
       const int lo = 32 * w;
       bits[w] = lo >= ncols ? 0u : (ncols - lo >= 32 ? 0xFFFFFFFFu : ((1u << (ncols - lo)) - 1u));
     }
-    if (lane == 0) counts[row] = ncols;
+    if (tid == 0) counts[row] = ncols;
     return;
   }
 
   // row max of the fast log scores (re-weighting against the top block)
   float lmax = -INFINITY;
-  for (int J = lane; J < ncols; J += 64) lmax = fmaxf(lmax, L[J]);
+  for (int J = tid; J < ncols; J += kSelThreads) lmax = fmaxf(lmax, L[J]);
   lmax = wave_max(lmax);
+  if (lane == 0) redf[wave] = lmax;
+  __syncthreads();
+  lmax = redf[0];
+#pragma unroll
+  for (int w = 1; w < kSelThreads / 64; ++w) lmax = fmaxf(lmax, redf[w]);
   const float lna = __logf(alpha);
   const float thr = lna + lmax;
 
-  // any entry close enough to the threshold to need exact evaluation?
-  bool need = false;
-  for (int J = lane; J < ncols; J += 64) {
-    const bool forced = J < n_sink || I - J < n_local;
-    need |= (!forced && fabsf(L[J] - thr) <= kGuard);
+  // pass 1: fast decisions and candidate bitmaps
+  int need_l = 0;
+  for (int base = 64 * wave; base < 32 * nw_row; base += kSelThreads) {
+    const int J = base + lane;
+    bool kp = false, ct = false, cm = false;
+    if (J < ncols) {
+      const float l = L[J];
+      const bool forced = J < n_sink || I - J < n_local;
+      kp = forced || l >= thr;
+      ct = !forced && fabsf(l - thr) <= kGuard;
+      cm = l >= lmax - kGuard;
+    }
+    const unsigned long long bk = __ballot(kp), bt = __ballot(ct), bm = __ballot(cm);
+    need_l |= bt != 0ull;
+    if (lane == 0) {
+      const int w = base >> 5;  // w + 1 <= kW (the arrays hold kW + 1 words)
+      keep_fast[w] = (uint32_t)bk;
+      keep_fast[w + 1] = (uint32_t)(bk >> 32);
+      cand_thr[w] = (uint32_t)bt;
+      cand_thr[w + 1] = (uint32_t)(bt >> 32);
+      cand_max[w] = (uint32_t)bm;
+      cand_max[w + 1] = (uint32_t)(bm >> 32);
+    }
   }
-  need = __any(need);
+  if (lane == 0) redi[wave] = need_l;
+  __syncthreads();
+  int need = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) need |= redi[w];
 
-  double ex_thr = 0.0;
+  // pass 2: exact evaluation (uniform loops over the candidate bitmaps)
   if (need) {
     const int len = cu[s + 1] - cu[s];
     const int nI = min(kBlock, len - I * kBlock);
@@ -147,56 +257,52 @@ __global__ __launch_bounds__(256) void decide_kernel(
     const float* kb = k_mean + ((int64_t)h * num_blocks + boff[s]) * kHeadDim;
     const double ref = (double)lmax;
     double emax = -INFINITY;
-    // exact maximum over every candidate for the row maximum
-    for (int base = 0; base < ncols; base += 64) {
-      const int J = base + lane;
-      const bool cand = J < ncols && L[J] >= lmax - kGuard;
-      unsigned long long m = __ballot(cand);
+    for (int w = 0; w < nw_row; ++w) {
+      uint32_t m = cand_max[w];
       while (m) {
-        const int b = __ffsll((long long)m) - 1;
-        m &= m - 1;
-        const double e = exact_score<QDT>(q, q_scale, kb + (int64_t)(base + b) * kHeadDim, hq,
-                                          group, h, tok0, nI, (double)softmax_scale, ref, lane);
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        const double e = exact_score_wg<QDT>(q, q_scale, kb + (int64_t)(32 * w + b) * kHeadDim, hq,
+                                             group, h, tok0, nI, (double)softmax_scale, ref, redd);
         emax = fmax(emax, e);
       }
     }
-    ex_thr = log((double)alpha) + emax;
+    const double ex_thr = log((double)alpha) + emax;
+    for (int w = 0; w < nw_row; ++w) {
+      uint32_t m = cand_thr[w];
+      uint32_t fix = 0u;
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        const double e = exact_score_wg<QDT>(q, q_scale, kb + (int64_t)(32 * w + b) * kHeadDim, hq,
+                                             group, h, tok0, nI, (double)softmax_scale, ref, redd);
+        if (e >= ex_thr) fix |= 1u << b;
+      }
+      if (tid == 0) keep_fix[w] = fix;
+    }
+    __syncthreads();
   }
 
-  int count = 0;
-  // every word of the row is written (blocks past the diagonal are zero)
-  for (int base = 0; base < 32 * words; base += 64) {
-    const int J = base + lane;
-    bool keep = false, recheck = false;
-    if (J < ncols) {
-      const bool forced = J < n_sink || I - J < n_local;
-      keep = forced || L[J] >= thr;
-      recheck = need && !forced && fabsf(L[J] - thr) <= kGuard;
+  // pass 3: every word of the row (blocks past the diagonal are zero)
+  int cnt = 0;
+  for (int w = tid; w < words; w += kSelThreads) {
+    uint32_t v = 0u;
+    if (w < nw_row) {
+      v = keep_fast[w];
+      if (need) v = (v & ~cand_thr[w]) | keep_fix[w];
     }
-    unsigned long long m = __ballot(recheck);
-    if (m) {
-      const int len = cu[s + 1] - cu[s];
-      const int nI = min(kBlock, len - I * kBlock);
-      const int64_t tok0 = (int64_t)cu[s] + (int64_t)I * kBlock;
-      const float* kb = k_mean + ((int64_t)h * num_blocks + boff[s]) * kHeadDim;
-      while (m) {
-        const int b = __ffsll((long long)m) - 1;
-        m &= m - 1;
-        const double e = exact_score<QDT>(q, q_scale, kb + (int64_t)(base + b) * kHeadDim, hq,
-                                          group, h, tok0, nI, (double)softmax_scale,
-                                          (double)lmax, lane);
-        if (lane == b) keep = e >= ex_thr;
-      }
-    }
-    const unsigned long long kb64 = __ballot(keep);
-    count += __popcll(kb64);
-    if (lane == 0) {
-      const int w = base >> 5;
-      bits[w] = (uint32_t)kb64;
-      if (w + 1 < words) bits[w + 1] = (uint32_t)(kb64 >> 32);
-    }
+    bits[w] = v;
+    cnt += __popc(v);
   }
-  if (lane == 0) counts[row] = count;
+  cnt = (int)wave_sum((float)cnt);
+  if (lane == 0) redi[wave] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) tot += redi[w];
+    counts[row] = tot;
+  }
 }
 
 // Exclusive scan of counts[nrows] -> row_ptr[nrows + 1] (one workgroup).
@@ -265,9 +371,9 @@ hipError_t launch_select(const Geometry& g, const int32_t* cu, const int32_t* bo
                          const float* q_scale, const float* k_mean, const float* scores,
                          float alpha, int n_sink, int n_local, uint32_t* keep_bits,
                          int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
-  const unsigned nwg = (unsigned)((g.num_rows + kRowsPerWg - 1) / kRowsPerWg);
+  const unsigned nwg = (unsigned)g.num_rows;
 #define FP_DEC(QD)                                                                              \
-  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(256), 0, st, cu, boff, g.num_seqs,     \
+  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, cu, boff, g.num_seqs,     \
                      g.hq, g.hkv, g.group, g.num_blocks, g.max_blocks, g.softmax_scale, q,        \
                      q_scale, k_mean, scores, alpha, n_sink, n_local, keep_bits, counts)
   if (g.qk_dtype == FP_BF16) FP_DEC(FP_BF16);
