@@ -565,6 +565,24 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     f32x16 sa[RC], sb[RC];
     bf16x8 pa[RC][2], pq[RC][2];
     float la[RC], lq[RC];
+    // Chunks that are masked for every row of this wave are skipped: in the
+    // diagonal tile the keys past the wave's last row, in a pooled tile the
+    // pooled keys past block I.  Such tiles run the chunks in plain order.
+    int nc = 4;
+    if constexpr (DIAG) nc = min(4, tbase / 32 + RC);
+    if constexpr (POOLED) nc = min(4, (I - kBlock * tile_index(t)) / 32 + 1);
+    if (nc < 4) {
+      for (int c = 0; c < nc; ++c) {
+        qk(c, sa);
+        const bool o1 = softmax(c, sa, pa, la);
+        settle(o1, sa, pa, la);
+        pv(c, pa);
+      }
+      publish_slot(t + 2, page_next, buf);
+      wait_vm();
+      __syncthreads();
+      return;
+    }
     qk(0, sa);
     __builtin_amdgcn_sched_barrier(0);
     qk(1, sb);
