@@ -227,6 +227,8 @@ def make_workload(spec: WorkloadSpec, threads: Optional[int] = None) -> Workload
     def fill(task):
         s, h = task
         L, t0 = seqlens[s], int(cu[s])
+        if L == 0:  # empty sequence: no tokens to draw
+            return
         n = math.ceil(L / B)
         blk = np.arange(L) // B
         rs = _stream(spec.seed, s, h, 0)

@@ -106,3 +106,32 @@ def test_full_size_config_sampled_parity(name, nrows):
                 assert lst[-1] == I and np.all(np.diff(lst) > 0) and lst[0] >= 0
                 assert set(range(min(2, I + 1))) <= set(lst.tolist())
                 assert set(range(max(0, I - 3), I + 1)) <= set(lst.tolist())
+
+
+def test_empty_sequences_in_batch():
+    """Zero-length sequences between and around real ones (cu_seqlens with
+    repeated offsets): they own no blocks, no lists and no output rows."""
+    log("case empty_mix")
+    w = make_workload(custom_spec(name="empty_mix", seqlens=(0, 300, 0, 129, 0), num_q_heads=4,
+                                  num_kv_heads=2, page_size=16, paging="roundrobin", seed=130))
+    g = run_gpu(w, 0.1)
+    compare(w, g, 0.1)
+
+
+def test_max_blocks_per_sequence():
+    """One sequence at the 8192-block limit (1,048,576 tokens; Hq=2 / Hkv=1,
+    pages of 128, permuted): the per-sequence LDS structures of discovery,
+    selection and attention at full size.  Pooled means everywhere; lists,
+    scores and outputs on sampled rows; structure of every list."""
+    log("case max_blocks_1m")
+    w = make_workload(custom_spec(name="max_blocks_1m", seqlens=(8192 * 128,), num_q_heads=2,
+                                  num_kv_heads=1, page_size=128, paging="permute", seed=131))
+    g = run_gpu(w, 0.1)
+    compare(w, g, 0.1, rows=sample_rows(w, 4), check_pool=True)
+    rp, ci = g["row_ptr"], g["col_idx"]
+    assert rp.shape[0] == 8192 + 1
+    for I in range(8192):
+        lst = ci[rp[I]:rp[I + 1]]
+        assert lst[-1] == I and np.all(np.diff(lst) > 0) and lst[0] >= 0
+        assert set(range(min(2, I + 1))) <= set(lst.tolist())
+        assert set(range(max(0, I - 3), I + 1)) <= set(lst.tolist())
