@@ -632,13 +632,48 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   for (int t = nkept; t < ntiles; ++t) iterate(t, std::true_type{}, std::false_type{});
 
   // ---- epilogue: O = acc / l, lse = m + log2(l) (natural log out) ----
+  if constexpr (kFp8) {
+    // direct stores (the e4m3 instances keep their register budget for the
+    // loops; the staged form below adds pressure that spills there)
+#pragma unroll
+    for (int rc = 0; rc < RC; ++rc) {
+      const float l_tot = l_run[rc] + __shfl_xor(l_run[rc], 32, 64);
+      const float inv = 1.f / l_tot;
+      if (col >= nvalid[rc]) continue;
+      const int64_t tok = tok0 + tbase + 32 * rc + col;
+      const int64_t obase = (tok * a.hq + hq_idx) * (int64_t)kHeadDim;
+#pragma unroll
+      for (int dc = 0; dc < 4; ++dc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * dc + 8 * j + 4 * half;
+          const float x0 = o[rc][dc][4 * j] * inv, x1 = o[rc][dc][4 * j + 1] * inv;
+          const float x2 = o[rc][dc][4 * j + 2] * inv, x3 = o[rc][dc][4 * j + 3] * inv;
+          if constexpr (ODT == FP_BF16) {
+            *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(a.out) + obase + d) =
+                f32x4_to_bf16x4(make_float4(x0, x1, x2, x3));
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + obase + d) = make_float4(x0, x1, x2, x3);
+          }
+        }
+      }
+      if (a.lse && half == 0) a.lse[(int64_t)hq_idx * a.total_tokens + tok] = (m_run[rc] + __log2f(l_tot)) * kLn2;
+    }
+    return;
+  }
+  // Each wave stages its rows in LDS (the tile buffers are free after the
+  // last barrier; every wave owns a region of its own, so no barrier is
+  // needed) with 16-byte chunks XOR-swizzled by row, then writes whole output
+  // rows: 16 bytes per lane, 4 (bf16) or 2 (fp32) rows per store instruction.
+  constexpr int kOutB = (ODT == FP_BF16) ? 2 : 4;                 // bytes per output element
+  constexpr int kRowChunks = kHeadDim * kOutB / 16;               // 16-byte chunks per row
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* stage = reinterpret_cast<uint8_t*>(&sm.k[0][0]) + wv * (32 * RC * kHeadDim * kOutB);
 #pragma unroll
   for (int rc = 0; rc < RC; ++rc) {
     const float l_tot = l_run[rc] + __shfl_xor(l_run[rc], 32, 64);
     const float inv = 1.f / l_tot;
-    if (col >= nvalid[rc]) continue;
-    const int64_t tok = tok0 + tbase + 32 * rc + col;
-    const int64_t obase = (tok * a.hq + hq_idx) * (int64_t)kHeadDim;
+    const int r = 32 * rc + col;  // row inside the wave's block of rows
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
 #pragma unroll
@@ -646,15 +681,35 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
         const int d = 32 * dc + 8 * j + 4 * half;
         const float x0 = o[rc][dc][4 * j] * inv, x1 = o[rc][dc][4 * j + 1] * inv;
         const float x2 = o[rc][dc][4 * j + 2] * inv, x3 = o[rc][dc][4 * j + 3] * inv;
+        const int byte = d * kOutB;              // within the row
+        const int ch = byte >> 4, in = byte & 15;
+        uint8_t* dst = stage + r * (kHeadDim * kOutB) + ((ch ^ (r & (kRowChunks - 1))) << 4) + in;
         if constexpr (ODT == FP_BF16) {
-          *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(a.out) + obase + d) =
-              f32x4_to_bf16x4(make_float4(x0, x1, x2, x3));
+          *reinterpret_cast<uint2*>(dst) = f32x4_to_bf16x4(make_float4(x0, x1, x2, x3));
         } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + obase + d) = make_float4(x0, x1, x2, x3);
+          *reinterpret_cast<float4*>(dst) = make_float4(x0, x1, x2, x3);
         }
       }
     }
-    if (a.lse && half == 0) a.lse[(int64_t)hq_idx * a.total_tokens + tok] = (m_run[rc] + __log2f(l_tot)) * kLn2;
+    if (a.lse && half == 0 && col < nvalid[rc])
+      a.lse[(int64_t)hq_idx * a.total_tokens + tok0 + tbase + r] = (m_run[rc] + __log2f(l_tot)) * kLn2;
+  }
+  // read back whole rows (the wave's own LDS writes are ordered before its reads)
+  constexpr int kRowsPerStore = 64 / kRowChunks;
+  int nrows_w = 0;  // valid rows of this wave (chunks fill in order)
+#pragma unroll
+  for (int rc = 0; rc < RC; ++rc) nrows_w += nvalid[rc];
+#pragma unroll
+  for (int it = 0; it < 32 * RC / kRowsPerStore; ++it) {
+    const int r = it * kRowsPerStore + lane / kRowChunks;
+    const int ch = lane % kRowChunks;
+    if (r < nrows_w) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * (kHeadDim * kOutB) +
+                                                      ((ch ^ (r & (kRowChunks - 1))) << 4));
+      const int64_t tok = tok0 + tbase + r;
+      uint8_t* gdst = reinterpret_cast<uint8_t*>(a.out) + ((tok * a.hq + hq_idx) * (int64_t)kHeadDim) * kOutB + ch * 16;
+      *reinterpret_cast<uint4*>(gdst) = v;
+    }
   }
 }
 
