@@ -189,7 +189,12 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
  * The g = Hq / Hkv query heads of a KV head are packed into shared K/V tiles
  * (PackGQA, V2 paper reading 4.2(1)); K/V tiles are gathered through the page
  * table without a contiguous copy (4.3).  QK^T runs on bf16 MFMA (fp8 e4m3
- * MFMA when qk_dtype == FP_E4M3), PV on bf16 MFMA; softmax in fp32.
+ * MFMA when qk_dtype == FP_E4M3), PV on bf16 MFMA; softmax in fp32.  Rows
+ * are scheduled by their tile count, most first (the list lengths decide the
+ * work, not the positions: V2 paper reading, KV-split section); the schedule
+ * is computed on the stream into the workspace, so the call stays free of
+ * host synchronisation.  A list entry outside [0, I] or a list longer than
+ * I + 1 gives unspecified output for that row but no out-of-bounds access.
  *
  * q, k_cache, v_cache, row_ptr, col_idx, k_mean, v_mean: inputs (k_mean /
  * v_mean may be NULL when mean_correction == 0).  out: output.  lse: output
