@@ -191,7 +191,8 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
  * table without a contiguous copy (4.3).  QK^T runs on bf16 MFMA (fp8 e4m3
  * MFMA when qk_dtype == FP_E4M3), PV on bf16 MFMA; softmax in fp32.  Rows
  * are scheduled by their tile count, most first (the list lengths decide the
- * work, not the positions: V2 paper reading, KV-split section); the schedule
+ * work, not the positions: "長文本推理越來越長但你的顯卡等不起…FlashPrefill
+ * V2", KV-split load-balancing section); the schedule
  * is computed on the stream into the workspace, so the call stays free of
  * host synchronisation.  A list entry outside [0, I] or a list longer than
  * I + 1 gives unspecified output for that row but no out-of-bounds access.
