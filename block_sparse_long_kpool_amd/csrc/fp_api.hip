@@ -87,7 +87,7 @@ int make_geometry(const fp_problem* p, Geometry* g) {
 
 struct DiscoverWs { int32_t* boff; u16* km16; };
 struct SelectWs { int32_t* boff; uint32_t* bits; int32_t* counts; };
-struct AttnWs { int32_t* boff; u16* km16; u16* vm16; int32_t* order; };
+struct AttnWs { int32_t* boff; u16* km16; u16* vm16; };
 
 size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
   char* b = reinterpret_cast<char*>(base);
@@ -116,7 +116,6 @@ size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
     w.boff = (int32_t*)take(boff_bytes);
     w.km16 = (u16*)take(pooled16);
     w.vm16 = (u16*)take(pooled16);
-    w.order = (int32_t*)take(sizeof(int32_t) * (size_t)g.num_rows);
     if (out) *reinterpret_cast<AttnWs*>(out) = w;
   } else {
     return 0;
@@ -259,12 +258,9 @@ int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache
   if ((st = hip_status(launch_attn_prep(g, p->cu_seqlens_dev, w.boff, mean_correction ? k_mean : nullptr,
                                         v_mean, w.km16, w.vm16, s), "attn prep")))
     return st;
-  if ((st = hip_status(launch_attn_sched(g, w.boff, row_ptr, mean_correction ? 1 : 0, w.order, s),
-                       "attn schedule")))
-    return st;
   return hip_status(launch_attn(g, p->cu_seqlens_dev, w.boff, p->page_table_dev, q, k_cache, v_cache,
                                 p->q_scale_dev, p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
-                                w.order, mean_correction ? 1 : 0, out, lse, s),
+                                mean_correction ? 1 : 0, out, lse, s),
                     "attn");
 }
 

@@ -67,7 +67,6 @@ struct AttnArgs {
   const int32_t* col_idx;
   const u16* km16;
   const u16* vm16;
-  const int32_t* order;  // CSR rows by descending tile count
   void* out;
   float* lse;
   int64_t num_blocks;
@@ -124,21 +123,17 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // ---- work item (row, pack) ----
-  // Rows are taken in the scheduled order (most tiles first) and spread over
-  // the XCDs round robin (workgroups are dispatched to the XCDs round robin);
-  // the packs of a row are consecutive workgroups of one XCD, so the g/2
-  // workgroups that share a row's K/V tiles run there at about the same time
-  // and hit its L2.
-  const int xcd = blockIdx.x % kAttnXcds;
-  const int kq = blockIdx.x / kAttnXcds;
+  // ---- work item: XCD-grouped (row, pack), heaviest rows first ----
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int kq = b >> 3;
   const int pack = kq % a.packs;
-  const int64_t row_rank = (int64_t)(kq / a.packs) * kAttnXcds + xcd;
+  const int64_t row_ord = (int64_t)(kq / a.packs) * 8 + xcd;
   const int64_t nrows = (int64_t)a.hkv * a.num_blocks;
-  if (row_rank >= nrows) return;
-  const int64_t row = a.order[row_rank];
-  const int h = (int)(row / a.num_blocks);
-  const int gb = (int)(row % a.num_blocks);
+  if (row_ord >= nrows) return;
+  const int h = (int)(row_ord % a.hkv);
+  const int gb = (int)(a.num_blocks - 1 - row_ord / a.hkv);
+  const int64_t row = (int64_t)h * a.num_blocks + gb;
   const int s = find_seq(a.boff, a.num_seqs, gb);
   const int I = gb - a.boff[s];
   const int len = a.cu[s + 1] - a.cu[s];
@@ -664,7 +659,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       }
       if (a.lse && half == 0) a.lse[(int64_t)hq_idx * a.total_tokens + tok] = (m_run[rc] + __log2f(l_tot)) * kLn2;
     }
-  } else {
+    return;
+  }
   // Each wave stages its rows in LDS (the tile buffers are free after the
   // last barrier; every wave owns a region of its own, so no barrier is
   // needed) with 16-byte chunks XOR-swizzled by row, then writes whole output
@@ -715,7 +711,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint4*>(gdst) = v;
     }
   }
-  }
 }
 
 // boff (last block of the grid) and bf16 copies of the pooled keys / values.
@@ -757,55 +752,6 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const int32_t* __restric
   *reinterpret_cast<uint2*>(vm16 + i) = f32x4_to_bf16x4(y);
 }
 
-// Work order for the persistent attention grid (one workgroup of 1024
-// threads): rows are counting-sorted by their tile count (kept blocks plus, with
-// correction, the pooled tiles up to block I), most tiles first, into order[];
-// the order inside one count bin is unspecified (every row is computed
-// independently, so results do not depend on it).
-constexpr int kSchedBins = 1024;
-__global__ __launch_bounds__(1024) void attn_sched_kernel(const int32_t* __restrict__ boff, int num_seqs,
-                                                         int64_t num_blocks, int hkv,
-                                                         const int32_t* __restrict__ row_ptr,
-                                                         int correction, int32_t* __restrict__ order) {
-  __shared__ int hist[kSchedBins];
-  const int tid = threadIdx.x;
-  const int64_t nrows = (int64_t)hkv * num_blocks;
-  for (int i = tid; i < kSchedBins; i += 1024) hist[i] = 0;
-  __syncthreads();
-  auto bin_of = [&](int64_t r) {
-    const int gb = (int)(r % num_blocks);
-    const int s = find_seq(boff, num_seqs, gb);
-    const int I = gb - boff[s];
-    const int nk = min(max(row_ptr[r + 1] - row_ptr[r], 0), I + 1);
-    const int cost = nk + (correction ? (I >> 7) + 1 : 0);
-    return kSchedBins - 1 - min(kSchedBins - 1, cost >> 3);  // bin 0 = most tiles
-  };
-  for (int64_t r = tid; r < nrows; r += 1024) atomicAdd(&hist[bin_of(r)], 1);
-  __syncthreads();
-  if (tid < 64) {  // exclusive scan over the bins, one wave (16 bins per lane)
-    int v[kSchedBins / 64];
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < kSchedBins / 64; ++j) {
-      v[j] = hist[tid * (kSchedBins / 64) + j];
-      sum += v[j];
-    }
-    int x = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (tid >= o) x += y;
-    }
-    int start = x - sum;
-#pragma unroll
-    for (int j = 0; j < kSchedBins / 64; ++j) {
-      hist[tid * (kSchedBins / 64) + j] = start;
-      start += v[j];
-    }
-  }
-  __syncthreads();
-  for (int64_t r = tid; r < nrows; r += 1024) order[atomicAdd(&hist[bin_of(r)], 1)] = (int32_t)r;
-}
-
 }  // namespace
 
 hipError_t launch_attn_prep(const Geometry& g, const int32_t* cu, int32_t* boff, const float* k_mean,
@@ -817,18 +763,10 @@ hipError_t launch_attn_prep(const Geometry& g, const int32_t* cu, int32_t* boff,
   return hipGetLastError();
 }
 
-hipError_t launch_attn_sched(const Geometry& g, const int32_t* boff, const int32_t* row_ptr,
-                             int correction, int32_t* order, hipStream_t st) {
-  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(1024), 0, st, boff, g.num_seqs, g.num_blocks, g.hkv,
-                     row_ptr, correction, order);
-  return hipGetLastError();
-}
-
 hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff, const int32_t* page_table,
                        const void* q, const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx, const u16* km16,
-                       const u16* vm16, const int32_t* order, int correction, void* out,
-                       float* lse, hipStream_t st) {
+                       const u16* vm16, int correction, void* out, float* lse, hipStream_t st) {
   AttnArgs a;
   a.cu = cu;
   a.boff = boff;
@@ -842,7 +780,6 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   a.col_idx = col_idx;
   a.km16 = km16;
   a.vm16 = vm16;
-  a.order = order;
   a.out = out;
   a.lse = lse;
   a.num_blocks = g.num_blocks;
@@ -857,7 +794,7 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   a.correction = correction;
   a.softmax_scale = g.softmax_scale;
   const int64_t rows = (int64_t)g.hkv * g.num_blocks;
-  const unsigned grid = (unsigned)(((rows + kAttnXcds - 1) / kAttnXcds) * kAttnXcds * a.packs);
+  const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs);
   const size_t shm = sizeof(SharedMem);
 #define FP_ATTN(QD, VD, OD)                                                                    \
   do {                                                                                         \

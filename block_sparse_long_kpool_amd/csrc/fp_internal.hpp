@@ -156,17 +156,10 @@ hipError_t launch_attn_prep(const Geometry& g, const int32_t* cu, int32_t* boff,
                             const float* k_mean, const float* v_mean, u16* km16, u16* vm16,
                             hipStream_t st);
 
-// Work order of the attention grid: CSR rows sorted by tile count
-// (descending) into order[num_rows]; items are spread over kAttnXcds XCDs.
-constexpr int kAttnXcds = 8;
-hipError_t launch_attn_sched(const Geometry& g, const int32_t* boff, const int32_t* row_ptr,
-                             int correction, int32_t* order, hipStream_t st);
-
 hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff,
                        const int32_t* page_table, const void* q, const void* k_cache,
                        const void* v_cache, const float* q_scale, const float* k_scale,
                        const int32_t* row_ptr, const int32_t* col_idx, const u16* km16,
-                       const u16* vm16, const int32_t* order, int correction, void* out,
-                       float* lse, hipStream_t st);
+                       const u16* vm16, int correction, void* out, float* lse, hipStream_t st);
 
 }  // namespace fp

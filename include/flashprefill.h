@@ -190,12 +190,11 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
  * (PackGQA, V2 paper reading 4.2(1)); K/V tiles are gathered through the page
  * table without a contiguous copy (4.3).  QK^T runs on bf16 MFMA (fp8 e4m3
  * MFMA when qk_dtype == FP_E4M3), PV on bf16 MFMA; softmax in fp32.  Rows
- * are scheduled by their tile count, most first (the list lengths decide the
- * work, not the positions: "長文本推理越來越長但你的顯卡等不起…FlashPrefill
- * V2", KV-split load-balancing section); the schedule
- * is computed on the stream into the workspace, so the call stays free of
- * host synchronisation.  A list entry outside [0, I] or a list longer than
- * I + 1 gives unspecified output for that row but no out-of-bounds access.
+ * are launched last query block first (the work of a row grows with its
+ * position: its pooled tiles and, on average, its list), KV heads
+ * interleaved, the g/2 workgroups of a row together on one XCD.  A list entry
+ * outside [0, I] or a list longer than I + 1 gives unspecified output for
+ * that row but no out-of-bounds access.
  *
  * q, k_cache, v_cache, row_ptr, col_idx, k_mean, v_mean: inputs (k_mean /
  * v_mean may be NULL when mean_correction == 0).  out: output.  lse: output
