@@ -5,12 +5,12 @@
 // so the attention loop walks only them).
 //
 // Three kernels:
-//   decide  one wave per CSR row: re-weight (subtract the row max of the log
-//           scores), threshold, forced blocks -> keep bitmask + count.
-//           Entries whose fast (bf16) score lies within kGuard of the
-//           threshold are re-evaluated in float64 from q and k_mean, with
-//           the row maximum re-evaluated the same way, so that every
-//           decision matches exact arithmetic.
+//   decide  one workgroup (4 waves) per CSR row: re-weight (subtract the row
+//           max of the log scores), threshold, forced blocks -> keep bitmask
+//           + count.  Entries whose fast (bf16) score lies within kGuard of
+//           the threshold are re-evaluated in float64 from q and k_mean by
+//           the whole workgroup, with the row maximum re-evaluated the same
+//           way, so that every decision matches exact arithmetic.
 //   scan    one workgroup: exclusive prefix sum of the counts -> row_ptr.
 //   compact one wave per row: wavefront ballot + popcount prefix writes the
 //           kept block indices in ascending order.
