@@ -16,7 +16,8 @@ Sources (the pages that describe the method), cited below by tag + section:
        2026-08-22): section 四 (two-stage flow, B=128, alpha=0.1, 256 sinks,
        512 local), 4.1 (block-mean correction sums), 4.3 (paged KV).
   [V2a] "長文本推理越來越長但你的顯卡等不起…FlashPrefill V2" (animattoys.com):
-       mean-correction section, CSR / paged-KV section (address rule).
+       mean-correction section, CSR / paged-KV section (address rule),
+       chunked-prefill (分塊預填充) passage (selection redone per chunk).
 
 Every step is computed in float64 on the exact values the GPU consumes:
 bf16 bit patterns and e4m3 codes are decoded exactly (e4m3 code x fp32 scale
@@ -51,6 +52,12 @@ design notes):
   R12 index lists hold block indices inside the sequence, ascending.
   R19 an entry whose Shat lies within 1e-5 * alpha of alpha is "in band":
      both decisions are correct there; such entries are flagged.
+  R20 chunked prefill ([V2a] chunked-prefill passage): a chunk's queries are
+     positions ctx .. ctx + qlen - 1 of a sequence whose first ctx tokens
+     (a multiple of B) are already cached.  Pooling covers every cached key
+     block; only the chunk's query blocks are scored, selected and attended,
+     each exactly as the same block of the whole prompt would be (sinks,
+     window and causality in positions counted from the sequence start).
 """
 
 from __future__ import annotations
@@ -138,6 +145,12 @@ class OracleProblem:
     q_scale: Optional[np.ndarray] = None
     k_scale: Optional[np.ndarray] = None
     softmax_scale: Optional[float] = None
+    # Chunked prefill ([V2a] chunked-prefill passage): ctx_lens[s] tokens of
+    # sequence s are already in the KV cache; the queries of this call are the
+    # positions ctx .. ctx + qlen - 1 and only their blocks are scored,
+    # selected and attended (reading R20: ctx is a multiple of B, so every
+    # query block is a whole block of the sequence).  None: whole prompts.
+    ctx_lens: Optional[np.ndarray] = None
 
     @classmethod
     def from_workload(cls, w) -> "OracleProblem":
@@ -145,7 +158,7 @@ class OracleProblem:
                    page_table=w.page_table, cu_seqlens=w.cu_seqlens,
                    qk_dtype=w.spec.qk_dtype, v_dtype=w.spec.v_dtype,
                    block_size=w.spec.block_size, q_scale=w.q_scale,
-                   k_scale=w.k_scale)
+                   k_scale=w.k_scale, ctx_lens=getattr(w, "ctx_lens", None))
 
     @property
     def num_seqs(self) -> int:
@@ -171,15 +184,36 @@ class OracleProblem:
     def scale(self) -> float:
         return self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.d)
 
-    def seqlen(self, s: int) -> int:
+    def ctx(self, s: int) -> int:
+        return 0 if self.ctx_lens is None else int(self.ctx_lens[s])
+
+    def qlen(self, s: int) -> int:
         return int(self.cu_seqlens[s + 1] - self.cu_seqlens[s])
+
+    def seqlen(self, s: int) -> int:
+        """Tokens in the KV cache of sequence s (cached prefix + queries)."""
+        return self.ctx(s) + self.qlen(s)
 
     def nblocks(self, s: int) -> int:
         return -(-self.seqlen(s) // self.block_size)
 
+    def query_blocks(self, s: int) -> range:
+        return range(self.ctx(s) // self.block_size, self.nblocks(s))
+
     def block_offsets(self) -> np.ndarray:
+        """Pooled-row offsets (key blocks) per sequence."""
         n = [self.nblocks(s) for s in range(self.num_seqs)]
         return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+
+    def query_block_offsets(self) -> np.ndarray:
+        """Score / CSR row offsets (query blocks) per sequence."""
+        n = [len(self.query_blocks(s)) for s in range(self.num_seqs)]
+        return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+
+    def row_index(self, h: int, s: int, I: int) -> int:
+        """Library row of (KV head, sequence, query block)."""
+        qoff = self.query_block_offsets()
+        return h * int(qoff[-1]) + int(qoff[s]) + I - self.ctx(s) // self.block_size
 
     def _paged_rows(self, cache: np.ndarray, s: int, h: int, pos: np.ndarray) -> np.ndarray:
         # [V2a] paged-KV section / [V2] 4.3: a token's address is the base of
@@ -202,8 +236,9 @@ class OracleProblem:
         return decode_storage(self._paged_rows(self.v_cache, s, h, pos), self.v_dtype)
 
     def queries(self, s: int, heads: Sequence[int], pos: np.ndarray) -> np.ndarray:
-        """float64 [len(heads), len(pos), d]."""
-        t = int(self.cu_seqlens[s]) + pos
+        """float64 [len(heads), len(pos), d]; pos: positions in the sequence
+        (cached prefix included), all >= ctx(s)."""
+        t = int(self.cu_seqlens[s]) + pos - self.ctx(s)
         raw = self.q[t][:, list(heads), :]
         if self.qk_dtype == "e4m3":
             vals = decode_e4m3(raw) * np.asarray(self.q_scale, np.float32)[list(heads)] \
@@ -346,11 +381,9 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
     decoded keys/values and pooled blocks of the last (sequence, kv head).
     """
     B = prob.block_size
-    boff = prob.block_offsets()
-    nblk = int(boff[-1])
     if rows is None:
         rows = [(h, s, I) for h in range(prob.hkv) for s in range(prob.num_seqs)
-                for I in range(prob.nblocks(s))]
+                for I in prob.query_blocks(s)]
     if cache is None:
         cache = {}
 
@@ -379,7 +412,7 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
             use = kept
             if given_csr is not None:
                 rp, ci = given_csr
-                r = h * nblk + int(boff[s]) + I
+                r = prob.row_index(h, s, I)
                 use = np.asarray(ci[rp[r]:rp[r + 1]], dtype=np.int64)
             out, lse = attend_block(qg, K, V, km, vm, cnt, use, I, B, prob.scale, correction)
             res["out"], res["lse"] = out, lse
@@ -408,15 +441,14 @@ def pooled_all(prob: OracleProblem):
 
 def csr_from_results(prob: OracleProblem, results: dict):
     """Library-order CSR (rows (h, s, I)) from a full run_pipeline result."""
-    boff = prob.block_offsets()
-    nblk = int(boff[-1])
-    counts = np.zeros(prob.hkv * nblk, dtype=np.int64)
+    nq = int(prob.query_block_offsets()[-1])
+    counts = np.zeros(prob.hkv * nq, dtype=np.int64)
     lists = {}
     for (h, s, I), r in results.items():
-        row = h * nblk + int(boff[s]) + I
+        row = prob.row_index(h, s, I)
         lists[row] = r["kept"]
         counts[row] = len(r["kept"])
-    row_ptr = np.zeros(prob.hkv * nblk + 1, dtype=np.int64)
+    row_ptr = np.zeros(prob.hkv * nq + 1, dtype=np.int64)
     row_ptr[1:] = np.cumsum(counts)
     col = np.zeros(int(row_ptr[-1]), dtype=np.int64)
     for row, kept in lists.items():

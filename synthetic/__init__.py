@@ -11,6 +11,7 @@ from .workloads import (  # noqa: F401
     CONFIGS,
     Workload,
     WorkloadSpec,
+    chunk_view,
     make_workload,
     spec_for,
     custom_spec,

@@ -120,10 +120,33 @@ class Workload:
     q_scale: Optional[np.ndarray] = None  # float32 [Hq] (e4m3 only)
     k_scale: Optional[np.ndarray] = None  # float32 [Hkv] (e4m3 only)
     extra: dict = field(default_factory=dict)
+    # tokens per sequence already in the KV cache before q (chunked prefill);
+    # None: q covers whole prompts
+    ctx_lens: Optional[np.ndarray] = None
 
     @property
     def num_pages(self) -> int:
         return int(self.k_cache.shape[0])
+
+
+def chunk_view(w: Workload, ctx_lens) -> Workload:
+    """The same prompts served in a later chunk: the first ctx_lens[s] tokens
+    of sequence s count as already cached (same K/V cache and page table),
+    and q holds only the remaining tokens.  No values are changed."""
+    ctx = np.asarray([int(x) for x in ctx_lens], dtype=np.int32)
+    cu = w.cu_seqlens
+    if len(ctx) != len(cu) - 1:
+        raise ValueError("one ctx length per sequence")
+    lens = np.diff(cu)
+    if np.any(ctx < 0) or np.any(ctx > lens) or np.any(ctx % w.spec.block_size):
+        raise ValueError("ctx lengths must be multiples of the block size within each sequence")
+    rows = np.concatenate([np.arange(cu[s] + ctx[s], cu[s + 1]) for s in range(len(ctx))])
+    qcu = np.zeros_like(cu)
+    qcu[1:] = np.cumsum(lens - ctx)
+    return Workload(spec=replace(w.spec, name=w.spec.name + "_chunk"),
+                    q=np.ascontiguousarray(w.q[rows.astype(np.int64)]), k_cache=w.k_cache,
+                    v_cache=w.v_cache, page_table=w.page_table, cu_seqlens=qcu.astype(np.int32),
+                    q_scale=w.q_scale, k_scale=w.k_scale, ctx_lens=ctx)
 
 
 # --------------------------------------------------------------------------
