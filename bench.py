@@ -83,26 +83,40 @@ def copy_calibration(mib, reps):
     print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
 
 
-def causal_pairs(seqlens, B=128):
-    """Causal (query, key) pairs per query head."""
-    return int(sum(L * (L + 1) // 2 for L in seqlens))
+def causal_pairs(seqlens, B=128, ctx=None):
+    """Causal (query, key) pairs per query head (query positions ctx .. L-1)."""
+    ctx = ctx or [0] * len(seqlens)
+    return int(sum(L * (L + 1) // 2 - c * (c + 1) // 2 for L, c in zip(seqlens, ctx)))
 
 
-def kept_pairs(row_ptr, col_idx, spec):
+def causal_blocks(seqlens, hkv, B=128, ctx=None):
+    """Causal (query block, key block) entries over the query blocks."""
+    ctx = ctx or [0] * len(seqlens)
+    tot = 0
+    for L, c in zip(seqlens, ctx):
+        n, i0 = -(-L // B), c // B
+        tot += n * (n + 1) // 2 - i0 * (i0 + 1) // 2
+    return hkv * tot
+
+
+def kept_pairs(row_ptr, col_idx, spec, ctx=None):
     """Kept query-key pairs summed over query heads, and the mean-correction
     (query row, pruned block) pairs, from the CSR lists (host arithmetic on
-    the index lists, for reporting only)."""
+    the index lists, for reporting only).  ctx: cached prefix per sequence
+    (chunked prefill; rows cover the query blocks only)."""
     B, g = spec.block_size, spec.group
-    boff = np.concatenate([[0], np.cumsum([-(-L // B) for L in spec.seqlens])])
-    nblk = int(boff[-1])
+    ctx = ctx or [0] * len(spec.seqlens)
+    nq = [-(-L // B) - c // B for L, c in zip(spec.seqlens, ctx)]
+    qoff = np.concatenate([[0], np.cumsum(nq)])
+    nrow = int(qoff[-1])
     kept = 0
     corr = 0
     for h in range(spec.num_kv_heads):
         for s, L in enumerate(spec.seqlens):
-            n = -(-L // B)
+            n, i0 = -(-L // B), ctx[s] // B
             cnt = np.minimum(B, L - np.arange(n) * B)
-            for I in range(n):
-                r = h * nblk + int(boff[s]) + I
+            for I in range(i0, n):
+                r = h * nrow + int(qoff[s]) + I - i0
                 J = col_idx[row_ptr[r]:row_ptr[r + 1]]
                 nI = int(cnt[I])
                 off = J[J < I]
@@ -111,12 +125,14 @@ def kept_pairs(row_ptr, col_idx, spec):
     return kept * g, corr * g
 
 
-def gpu_setup(spec, threads=None):
+def gpu_setup(spec, threads=None, ctx=None):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
-    from synthetic import make_workload
+    from synthetic import chunk_view, make_workload
     t0 = time.time()
     w = make_workload(spec, threads=threads)
+    if ctx is not None:
+        w = chunk_view(w, ctx)
     t_gen = time.time() - t0
     db = upload(w, "cuda")
     pipe = Pipeline(db)
@@ -207,6 +223,9 @@ def main():
                     help="also time the alpha sweep x correction (written to --sweep-out)")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-ctx", type=int, default=None, metavar="TOKENS",
+                    help="chunked prefill: the first TOKENS tokens of every prompt are already "
+                         "cached (a multiple of 128); the step processes the rest")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration)")
@@ -228,20 +247,21 @@ def main():
 
     spec = spec_for(args.workload)
     correction = not args.no_correction
-    w, pipe, t_gen = gpu_setup(spec)
+    ctx = None if args.chunk_ctx is None else [min(args.chunk_ctx, L) // 128 * 128
+                                               for L in spec.seqlens]
+    w, pipe, t_gen = gpu_setup(spec, ctx=ctx)
     print(f"# generated {spec.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
     t = time_steps(pipe, args.alpha, correction, args.steps, args.warmup)
     rp, ci = pipe.csr()
-    kp, cp = kept_pairs(rp, ci, spec)
+    kp, cp = kept_pairs(rp, ci, spec, ctx)
     d = spec.head_dim
     eff = 4 * d * kp / (t["step_ms"] * 1e-3) / 1e12
     attn_flop = 4 * d * (kp + (cp if correction else 0))
     achieved = attn_flop / (t["attn_ms"] * 1e-3) / 1e12
     peak = attn_peak(spec, kp, cp, correction)
-    causal = causal_pairs(spec.seqlens) * spec.num_q_heads
+    causal = causal_pairs(spec.seqlens, ctx=ctx) * spec.num_q_heads
     nrows = int(rp.shape[0] - 1)
-    causal_blocks = spec.num_kv_heads * sum((-(-L // 128)) * (-(-L // 128) + 1) // 2
-                                            for L in spec.seqlens)
+    cblocks = causal_blocks(spec.seqlens, spec.num_kv_heads, ctx=ctx)
     line = {
         "metric": "sparse prefill attn ms + effective TFLOP/s (% MFMA peak) at 128K, bf16/fp8",
         "value": round(eff, 3),
@@ -274,7 +294,7 @@ def main():
         "pct_peak": round(100 * eff / attn_peak(spec, kp, 0, False), 2),
         "discovery_selection_frac": round((t["discover_ms"] + t["select_ms"]) / t["step_ms"], 4),
         "density": {
-            "block": round(int(rp[-1]) / causal_blocks, 5),
+            "block": round(int(rp[-1]) / cblocks, 5),
             "pair": round(kp / causal, 5),
             "csr_bytes": int(4 * (rp.shape[0] + rp[-1])),
             "rows": nrows,
@@ -293,6 +313,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if ctx is not None:
+        line["config"]["chunk"] = {"cached_tokens": ctx, "query_tokens":
+                                   [L - c for L, c in zip(spec.seqlens, ctx)]}
+        line["roofline"]["traffic"] = None
     if args.sweep:
         os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
         with open(args.sweep_out, "w") as f:
@@ -300,14 +324,14 @@ def main():
                 for corr in (True, False):
                     ts = time_steps(pipe, a, corr, max(3, args.steps // 2), 1)
                     r2, c2 = pipe.csr()
-                    k2, q2 = kept_pairs(r2, c2, spec)
+                    k2, q2 = kept_pairs(r2, c2, spec, ctx)
                     rec = dict(workload=spec.name, alpha=a, correction=corr,
-                               block_density=int(r2[-1]) / causal_blocks,
+                               block_density=int(r2[-1]) / cblocks,
                                pair_density=k2 / causal,
                                eff_tflops=4 * d * k2 / (ts["step_ms"] * 1e-3) / 1e12, **ts)
                     f.write(json.dumps(rec) + "\n")
                     print("# sweep " + json.dumps(rec), file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and ctx is None:
         line["cpu_baseline"] = cpu_baseline(w, args.alpha, correction, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)
 

@@ -19,7 +19,8 @@ FP_WS_DISCOVER, FP_WS_SELECT, FP_WS_ATTN = 0, 1, 2
 DTYPE_CODES = {"f32": FP_F32, "bf16": FP_BF16, "e4m3": FP_E4M3}
 
 EXPORTED = (
-    "fp_num_blocks", "fp_max_blocks", "fp_num_rows", "fp_scores_elems", "fp_csr_capacity",
+    "fp_num_blocks", "fp_num_query_blocks", "fp_max_blocks", "fp_num_rows", "fp_scores_elems",
+    "fp_csr_capacity",
     "fp_workspace_bytes", "fp_status_string", "fp_last_error",
     "fp_discover", "fp_select", "fp_sparse_attn_paged",
 )
@@ -50,6 +51,8 @@ class FpProblemC(ctypes.Structure):
         ("q_scale_dev", ctypes.c_void_p),
         ("k_scale_dev", ctypes.c_void_p),
         ("softmax_scale", ctypes.c_float),
+        ("ctx_lens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("ctx_lens_dev", ctypes.c_void_p),
     ]
 
 
@@ -70,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "fp_num_blocks": (i64, [P]),
+        "fp_num_query_blocks": (i64, [P]),
         "fp_max_blocks": (i32, [P]),
         "fp_num_rows": (i64, [P]),
         "fp_scores_elems": (i64, [P]),
@@ -120,13 +124,20 @@ class Problem:
     def __init__(self, cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int,
                  page_table, page_size: int, num_pages: int, qk_dtype: str, v_dtype: str,
                  out_dtype: str, cu_seqlens_dev=None, q_scale=None, k_scale=None,
-                 softmax_scale: float = 0.0, device=None):
+                 softmax_scale: float = 0.0, device=None, ctx_lens: Optional[Sequence[int]] = None):
         import torch
         self.device = device or page_table.device
         cu = [int(x) for x in cu_seqlens]
         self.cu_host = (ctypes.c_int32 * len(cu))(*cu)
         self.cu_dev = cu_seqlens_dev if cu_seqlens_dev is not None else \
             torch.tensor(cu, dtype=torch.int32, device=self.device)
+        # cached prefix per sequence (chunked prefill); None = whole prompts
+        self.ctx_host = None
+        self.ctx_dev = None
+        if ctx_lens is not None:
+            ctx = [int(x) for x in ctx_lens]
+            self.ctx_host = (ctypes.c_int32 * len(ctx))(*ctx)
+            self.ctx_dev = torch.tensor(ctx, dtype=torch.int32, device=self.device)
         self.page_table = page_table
         self.q_scale = q_scale
         self.k_scale = k_scale
@@ -151,6 +162,9 @@ class Problem:
         c.q_scale_dev = _ptr(q_scale)
         c.k_scale_dev = _ptr(k_scale)
         c.softmax_scale = softmax_scale
+        if self.ctx_host is not None:
+            c.ctx_lens_host = self.ctx_host
+            c.ctx_lens_dev = _ptr(self.ctx_dev)
         self.c = c
         self.lib = load_library()
 
@@ -167,6 +181,10 @@ class Problem:
     @property
     def num_blocks(self) -> int:
         return self._q(self.lib.fp_num_blocks)
+
+    @property
+    def num_query_blocks(self) -> int:
+        return self._q(self.lib.fp_num_query_blocks)
 
     @property
     def max_blocks(self) -> int:

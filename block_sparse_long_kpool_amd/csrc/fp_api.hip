@@ -52,17 +52,27 @@ int make_geometry(const fp_problem* p, Geometry* g) {
     return fail(FP_ERR_INVALID, "e4m3 inputs need q_scale_dev and k_scale_dev");
   const int32_t* cu = p->cu_seqlens_host;
   if (cu[0] != 0) return fail(FP_ERR_INVALID, "cu_seqlens[0] must be 0");
-  int64_t nblk = 0;
+  if ((p->ctx_lens_host == nullptr) != (p->ctx_lens_dev == nullptr))
+    return fail(FP_ERR_INVALID, "ctx_lens_host and ctx_lens_dev must both be set or both be NULL");
+  int64_t nblk = 0, nqblk = 0;
   int maxn = 0, maxlen = 0;
   for (int s = 0; s < p->num_seqs; ++s) {
-    const int len = cu[s + 1] - cu[s];
-    if (len < 0) return fail(FP_ERR_INVALID, "cu_seqlens must be nondecreasing (seq %d)", s);
+    const int qlen = cu[s + 1] - cu[s];
+    if (qlen < 0) return fail(FP_ERR_INVALID, "cu_seqlens must be nondecreasing (seq %d)", s);
+    const int c = p->ctx_lens_host ? p->ctx_lens_host[s] : 0;
+    if (c < 0 || c % kBlock)
+      return fail(FP_ERR_INVALID, "ctx_lens[%d] = %d must be a nonnegative multiple of 128", s, c);
+    if ((int64_t)c + qlen > (int64_t)kMaxBlocksPerSeq * kBlock)
+      return fail(FP_ERR_UNSUPPORTED, "sequence %d of %lld tokens exceeds the %d-block limit", s,
+                  (long long)c + qlen, kMaxBlocksPerSeq);
+    const int len = c + qlen;
     const int n = (len + kBlock - 1) / kBlock;
     nblk += n;
+    nqblk += n - c / kBlock;
     maxn = std::max(maxn, n);
     maxlen = std::max(maxlen, len);
   }
-  if (nblk < 1) return fail(FP_ERR_INVALID, "batch has no tokens");
+  if (nqblk < 1) return fail(FP_ERR_INVALID, "batch has no query tokens");
   if (maxn > kMaxBlocksPerSeq)
     return fail(FP_ERR_UNSUPPORTED, "sequence of %d blocks exceeds the %d-block limit", maxn, kMaxBlocksPerSeq);
   if ((int64_t)p->max_pages_per_seq * P < maxlen)
@@ -75,8 +85,9 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   g->page_size = P;
   g->max_pages = p->max_pages_per_seq;
   g->num_blocks = nblk;
+  g->num_qblocks = nqblk;
   g->max_blocks = maxn;
-  g->num_rows = nblk * p->num_kv_heads;
+  g->num_rows = nqblk * p->num_kv_heads;
   g->total_tokens = cu[p->num_seqs];
   g->qk_dtype = qk;
   g->v_dtype = vd;
@@ -85,9 +96,19 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   return FP_OK;
 }
 
-struct DiscoverWs { int32_t* boff; u16* km16; };
-struct SelectWs { int32_t* boff; uint32_t* bits; int32_t* counts; };
-struct AttnWs { int32_t* boff; u16* km16; u16* vm16; };
+struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; };
+struct SelectWs { int32_t* kboff; int32_t* qboff; uint32_t* bits; int32_t* counts; };
+struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; };
+
+SeqMap seq_map(const fp_problem* p, int32_t* kboff, int32_t* qboff) {
+  SeqMap m;
+  m.cu = p->cu_seqlens_dev;
+  m.ctx = p->ctx_lens_dev;
+  m.kboff = kboff;
+  m.qboff = qboff;
+  m.num_seqs = p->num_seqs;
+  return m;
+}
 
 size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
   char* b = reinterpret_cast<char*>(base);
@@ -101,19 +122,22 @@ size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
   const size_t pooled16 = sizeof(u16) * (size_t)g.hkv * (size_t)g.num_blocks * kHeadDim;
   if (which == FP_WS_DISCOVER) {
     DiscoverWs w;
-    w.boff = (int32_t*)take(boff_bytes);
+    w.kboff = (int32_t*)take(boff_bytes);
+    w.qboff = (int32_t*)take(boff_bytes);
     w.km16 = (u16*)take(2 * pooled16);  // hi part, then lo part
     if (out) *reinterpret_cast<DiscoverWs*>(out) = w;
   } else if (which == FP_WS_SELECT) {
     SelectWs w;
     const size_t words = (size_t)(g.max_blocks + 31) / 32;
-    w.boff = (int32_t*)take(boff_bytes);
+    w.kboff = (int32_t*)take(boff_bytes);
+    w.qboff = (int32_t*)take(boff_bytes);
     w.bits = (uint32_t*)take(sizeof(uint32_t) * words * (size_t)g.num_rows);
     w.counts = (int32_t*)take(sizeof(int32_t) * (size_t)g.num_rows);
     if (out) *reinterpret_cast<SelectWs*>(out) = w;
   } else if (which == FP_WS_ATTN) {
     AttnWs w;
-    w.boff = (int32_t*)take(boff_bytes);
+    w.kboff = (int32_t*)take(boff_bytes);
+    w.qboff = (int32_t*)take(boff_bytes);
     w.km16 = (u16*)take(pooled16);
     w.vm16 = (u16*)take(pooled16);
     if (out) *reinterpret_cast<AttnWs*>(out) = w;
@@ -147,6 +171,11 @@ int64_t fp_num_blocks(const fp_problem* p) {
   return make_geometry(p, &g) == FP_OK ? g.num_blocks : -1;
 }
 
+int64_t fp_num_query_blocks(const fp_problem* p) {
+  Geometry g;
+  return make_geometry(p, &g) == FP_OK ? g.num_qblocks : -1;
+}
+
 int32_t fp_max_blocks(const fp_problem* p) {
   Geometry g;
   return make_geometry(p, &g) == FP_OK ? g.max_blocks : -1;
@@ -167,8 +196,10 @@ int64_t fp_csr_capacity(const fp_problem* p) {
   if (make_geometry(p, &g) != FP_OK) return -1;
   int64_t c = 0;
   for (int s = 0; s < p->num_seqs; ++s) {
-    const int64_t n = (p->cu_seqlens_host[s + 1] - p->cu_seqlens_host[s] + kBlock - 1) / kBlock;
-    c += n * (n + 1) / 2;
+    const int64_t ctx = p->ctx_lens_host ? p->ctx_lens_host[s] : 0;
+    const int64_t n = (ctx + p->cu_seqlens_host[s + 1] - p->cu_seqlens_host[s] + kBlock - 1) / kBlock;
+    const int64_t i0 = ctx / kBlock;  // first query block
+    c += n * (n + 1) / 2 - i0 * (i0 + 1) / 2;
   }
   return c * g.hkv;
 }
@@ -205,12 +236,12 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const v
   DiscoverWs w;
   ws_layout(g, FP_WS_DISCOVER, ws, &w);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((st = hip_status(launch_plan(p->cu_seqlens_dev, g.num_seqs, w.boff, s), "plan"))) return st;
-  if ((st = hip_status(launch_pool(g, p->cu_seqlens_dev, w.boff, p->page_table_dev, k_cache, v_cache,
-                                   p->k_scale_dev, k_mean, v_mean, w.km16, s), "pool")))
+  const SeqMap m = seq_map(p, w.kboff, w.qboff);
+  if ((st = hip_status(launch_plan(m, s), "plan"))) return st;
+  if ((st = hip_status(launch_pool(g, m, p->page_table_dev, k_cache, v_cache, p->k_scale_dev,
+                                   k_mean, v_mean, w.km16, s), "pool")))
     return st;
-  return hip_status(launch_scores(g, p->cu_seqlens_dev, w.boff, q, p->q_scale_dev, w.km16,
-                                  block_scores, s), "scores");
+  return hip_status(launch_scores(g, m, q, p->q_scale_dev, w.km16, block_scores, s), "scores");
 }
 
 int fp_select(const fp_problem* p, const void* q, const float* k_mean, const float* block_scores,
@@ -234,9 +265,10 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean, const flo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int n_sink = (sink_tokens + kBlock - 1) / kBlock;
   const int n_local = std::max(1, (local_tokens + kBlock - 1) / kBlock);
-  if ((st = hip_status(launch_plan(p->cu_seqlens_dev, g.num_seqs, w.boff, s), "plan"))) return st;
-  return hip_status(launch_select(g, p->cu_seqlens_dev, w.boff, q, p->q_scale_dev, k_mean, block_scores,
-                                  alpha, n_sink, n_local, w.bits, w.counts, row_ptr, col_idx, s),
+  const SeqMap m = seq_map(p, w.kboff, w.qboff);
+  if ((st = hip_status(launch_plan(m, s), "plan"))) return st;
+  return hip_status(launch_select(g, m, q, p->q_scale_dev, k_mean, block_scores, alpha, n_sink,
+                                  n_local, w.bits, w.counts, row_ptr, col_idx, s),
                     "select");
 }
 
@@ -255,11 +287,12 @@ int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache
   AttnWs w;
   ws_layout(g, FP_WS_ATTN, ws, &w);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if ((st = hip_status(launch_attn_prep(g, p->cu_seqlens_dev, w.boff, mean_correction ? k_mean : nullptr,
-                                        v_mean, w.km16, w.vm16, s), "attn prep")))
+  const SeqMap m = seq_map(p, w.kboff, w.qboff);
+  if ((st = hip_status(launch_attn_prep(g, m, mean_correction ? k_mean : nullptr, v_mean, w.km16,
+                                        w.vm16, s), "attn prep")))
     return st;
-  return hip_status(launch_attn(g, p->cu_seqlens_dev, w.boff, p->page_table_dev, q, k_cache, v_cache,
-                                p->q_scale_dev, p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
+  return hip_status(launch_attn(g, m, p->page_table_dev, q, k_cache, v_cache, p->q_scale_dev,
+                                p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
                                 mean_correction ? 1 : 0, out, lse, s),
                     "attn");
 }

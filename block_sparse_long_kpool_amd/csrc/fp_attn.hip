@@ -55,8 +55,7 @@ constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
 constexpr int kAttnWaves = FP_ATTN_WAVES;
 
 struct AttnArgs {
-  const int32_t* cu;
-  const int32_t* boff;
+  SeqMap m;
   const int32_t* page_table;
   const void* q;
   const void* k_cache;
@@ -69,9 +68,10 @@ struct AttnArgs {
   const u16* vm16;
   void* out;
   float* lse;
-  int64_t num_blocks;
+  int64_t num_blocks;   // NK (pooled rows per KV head)
+  int64_t num_qblocks;  // NQ (CSR rows per KV head)
   int64_t total_tokens;
-  int num_seqs, max_pages, page_size;
+  int max_pages, page_size;
   int hq, hkv, group, packs;
   int correction;
   float softmax_scale;
@@ -129,17 +129,18 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int kq = b >> 3;
   const int pack = kq % a.packs;
   const int64_t row_ord = (int64_t)(kq / a.packs) * 8 + xcd;
-  const int64_t nrows = (int64_t)a.hkv * a.num_blocks;
+  const int64_t nrows = (int64_t)a.hkv * a.num_qblocks;
   if (row_ord >= nrows) return;
   const int h = (int)(row_ord % a.hkv);
-  const int gb = (int)(a.num_blocks - 1 - row_ord / a.hkv);
-  const int64_t row = (int64_t)h * a.num_blocks + gb;
-  const int s = find_seq(a.boff, a.num_seqs, gb);
-  const int I = gb - a.boff[s];
-  const int len = a.cu[s + 1] - a.cu[s];
-  const int nI = min(kBlock, len - I * kBlock);
-  const int64_t tok0 = (int64_t)a.cu[s] + (int64_t)I * kBlock;
-  const int64_t pooled_base = (int64_t)h * a.num_blocks + a.boff[s];
+  const int gq = (int)(a.num_qblocks - 1 - row_ord / a.hkv);
+  const int64_t row = (int64_t)h * a.num_qblocks + gq;
+  const QBlock qb = query_block(a.m, gq);
+  const int s = qb.s;
+  const int I = qb.I;
+  const int len = qb.klen;  // keys: cached prefix + this chunk
+  const int nI = qb.nI;
+  const int64_t tok0 = qb.tok0;
+  const int64_t pooled_base = (int64_t)h * a.num_blocks + qb.kb0;
   const int kbeg = a.row_ptr[row];
   // a valid list holds at most I + 1 blocks (the LDS tile list is sized for it)
   const int nkept = min(max(a.row_ptr[row + 1] - kbeg, 0), I + 1);
@@ -713,34 +714,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   }
 }
 
-// boff (last block of the grid) and bf16 copies of the pooled keys / values.
-__global__ __launch_bounds__(256) void attn_prep_kernel(const int32_t* __restrict__ cu, int num_seqs,
-                                                        int32_t* __restrict__ boff, const float* __restrict__ km,
+// Block offsets of the map (last block of the grid) and bf16 copies of the
+// pooled keys / values.
+__global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const float* __restrict__ km,
                                                         const float* __restrict__ vm, u16* __restrict__ km16,
                                                         u16* __restrict__ vm16, int64_t n) {
   if (blockIdx.x == gridDim.x - 1) {
-    __shared__ int buf[256];
-    __shared__ int carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base < num_seqs; base += 256) {
-      const int s = base + (int)threadIdx.x;
-      const int v = s < num_seqs ? (cu[s + 1] - cu[s] + kBlock - 1) / kBlock : 0;
-      buf[threadIdx.x] = v;
-      __syncthreads();
-      for (int o = 1; o < 256; o <<= 1) {
-        const int x = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
-        __syncthreads();
-        buf[threadIdx.x] += x;
-        __syncthreads();
-      }
-      const int c = carry;
-      if (s < num_seqs) boff[s] = c + buf[threadIdx.x] - v;
-      __syncthreads();
-      if (threadIdx.x == 255) carry = c + buf[255];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) boff[num_seqs] = carry;
+    plan_offsets(m);
     return;
   }
   if (km == nullptr) return;
@@ -754,22 +734,22 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const int32_t* __restric
 
 }  // namespace
 
-hipError_t launch_attn_prep(const Geometry& g, const int32_t* cu, int32_t* boff, const float* k_mean,
+hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_mean,
                             const float* v_mean, u16* km16, u16* vm16, hipStream_t st) {
   const int64_t n = (int64_t)g.hkv * g.num_blocks * kHeadDim;
   const unsigned conv = k_mean ? (unsigned)((n / 4 + 255) / 256) : 0u;
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(conv + 1), dim3(256), 0, st, cu, g.num_seqs, boff, k_mean,
-                     v_mean, km16, vm16, n);
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(conv + 1), dim3(256), 0, st, m, k_mean, v_mean, km16,
+                     vm16, n);
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff, const int32_t* page_table,
-                       const void* q, const void* k_cache, const void* v_cache, const float* q_scale,
-                       const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx, const u16* km16,
-                       const u16* vm16, int correction, void* out, float* lse, hipStream_t st) {
+hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_table, const void* q,
+                       const void* k_cache, const void* v_cache, const float* q_scale,
+                       const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
+                       const u16* km16, const u16* vm16, int correction, void* out, float* lse,
+                       hipStream_t st) {
   AttnArgs a;
-  a.cu = cu;
-  a.boff = boff;
+  a.m = m;
   a.page_table = page_table;
   a.q = q;
   a.k_cache = k_cache;
@@ -783,8 +763,8 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   a.out = out;
   a.lse = lse;
   a.num_blocks = g.num_blocks;
+  a.num_qblocks = g.num_qblocks;
   a.total_tokens = g.total_tokens;
-  a.num_seqs = g.num_seqs;
   a.max_pages = g.max_pages;
   a.page_size = g.page_size;
   a.hq = g.hq;
@@ -793,7 +773,7 @@ hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff
   a.packs = (g.group + 1) / 2;
   a.correction = correction;
   a.softmax_scale = g.softmax_scale;
-  const int64_t rows = (int64_t)g.hkv * g.num_blocks;
+  const int64_t rows = (int64_t)g.hkv * g.num_qblocks;
   const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs);
   const size_t shm = sizeof(SharedMem);
 #define FP_ATTN(QD, VD, OD)                                                                    \

@@ -28,12 +28,27 @@ struct Geometry {
   int num_seqs;
   int hq, hkv, group;
   int page_size, max_pages;
-  int64_t num_blocks;  // N = sum_s n_s
-  int max_blocks;      // n_max
-  int64_t num_rows;    // Hkv * N
-  int64_t total_tokens;  // T
+  int64_t num_blocks;    // NK = sum_s nk_s key blocks (pooled rows)
+  int64_t num_qblocks;   // NQ = sum_s nq_s query blocks (score / CSR rows per KV head)
+  int max_blocks;        // max_s nk_s
+  int64_t num_rows;      // Hkv * NQ
+  int64_t total_tokens;  // T (query tokens)
   int qk_dtype, v_dtype, out_dtype;
   float softmax_scale;
+};
+
+// Where the tokens and blocks of each sequence live (device pointers).  The
+// query tokens cu[s] .. cu[s+1]-1 are the positions ctx[s] .. ctx[s]+qlen-1
+// of sequence s, whose KV cache holds klen = ctx[s] + qlen tokens (ctx is 0
+// without a cached prefix, else a multiple of 128: chunked prefill).  Key
+// block J < nk = ceil(klen / 128) is pooled row kboff[s] + J; the query
+// blocks are I = ctx/128 .. nk-1, at rows qboff[s] + I - ctx/128.
+struct SeqMap {
+  const int32_t* cu;
+  const int32_t* ctx;  // NULL: no cached prefix
+  int32_t* kboff;      // [num_seqs + 1], written by launch_plan
+  int32_t* qboff;      // [num_seqs + 1]
+  int num_seqs;
 };
 
 // ---- device helpers -------------------------------------------------------
@@ -61,6 +76,69 @@ __device__ __forceinline__ int find_seq(const int* __restrict__ boff, int num_se
     if (boff[mid] <= gb) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// One query block (score / CSR row gq of a KV head): sequence, block index
+// I inside the sequence, its query-token count and first query-token row,
+// the sequence's key length and first pooled row.
+struct QBlock {
+  int s, I, nI, klen, kb0;
+  int64_t tok0;
+};
+__device__ __forceinline__ QBlock query_block(const SeqMap& m, int gq) {
+  QBlock r;
+  r.s = find_seq(m.qboff, m.num_seqs, gq);
+  const int c = m.ctx ? m.ctx[r.s] : 0;
+  const int local = gq - m.qboff[r.s];
+  r.I = c / kBlock + local;
+  r.klen = c + (m.cu[r.s + 1] - m.cu[r.s]);
+  r.nI = min(kBlock, r.klen - r.I * kBlock);
+  r.tok0 = (int64_t)m.cu[r.s] + (int64_t)local * kBlock;
+  r.kb0 = m.kboff[r.s];
+  return r;
+}
+
+// Both block prefixes of SeqMap, by one workgroup of 256 threads.
+__device__ __forceinline__ void plan_offsets(const SeqMap& m) {
+  __shared__ int bufk[256], bufq[256];
+  __shared__ int carry_k, carry_q;
+  if (threadIdx.x == 0) carry_k = carry_q = 0;
+  __syncthreads();
+  for (int base = 0; base < m.num_seqs; base += 256) {
+    const int s = base + (int)threadIdx.x;
+    int nk = 0, nq = 0;
+    if (s < m.num_seqs) {
+      const int c = m.ctx ? m.ctx[s] : 0;
+      nk = (c + m.cu[s + 1] - m.cu[s] + kBlock - 1) / kBlock;
+      nq = nk - c / kBlock;
+    }
+    bufk[threadIdx.x] = nk;
+    bufq[threadIdx.x] = nq;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int xk = (int)threadIdx.x >= o ? bufk[threadIdx.x - o] : 0;
+      const int xq = (int)threadIdx.x >= o ? bufq[threadIdx.x - o] : 0;
+      __syncthreads();
+      bufk[threadIdx.x] += xk;
+      bufq[threadIdx.x] += xq;
+      __syncthreads();
+    }
+    const int ck = carry_k, cq = carry_q;
+    if (s < m.num_seqs) {
+      m.kboff[s] = ck + bufk[threadIdx.x] - nk;
+      m.qboff[s] = cq + bufq[threadIdx.x] - nq;
+    }
+    __syncthreads();
+    if (threadIdx.x == 255) {
+      carry_k = ck + bufk[255];
+      carry_q = cq + bufq[255];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    m.kboff[m.num_seqs] = carry_k;
+    m.qboff[m.num_seqs] = carry_q;
+  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -134,32 +212,29 @@ __device__ __forceinline__ void interleave() {
 
 // ---- launchers (one per translation unit) ---------------------------------
 
-// Block offsets boff[num_seqs + 1] from cu_seqlens (prefix of ceil(len/128)).
-hipError_t launch_plan(const int32_t* cu_seqlens, int num_seqs, int32_t* boff, hipStream_t st);
+// Block offsets kboff / qboff of the map (one workgroup).
+hipError_t launch_plan(const SeqMap& m, hipStream_t st);
 
-hipError_t launch_pool(const Geometry& g, const int32_t* cu, const int32_t* boff,
-                       const int32_t* page_table, const void* k_cache, const void* v_cache,
-                       const float* k_scale, float* k_mean, float* v_mean,
-                       u16* k_mean_bf16, hipStream_t st);
+hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
+                       const void* k_cache, const void* v_cache, const float* k_scale,
+                       float* k_mean, float* v_mean, u16* k_mean_bf16, hipStream_t st);
 
-hipError_t launch_scores(const Geometry& g, const int32_t* cu, const int32_t* boff,
-                         const void* q, const float* q_scale, const u16* k_mean_bf16,
-                         float* scores, hipStream_t st);
+hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
+                         const u16* k_mean_bf16, float* scores, hipStream_t st);
 
-hipError_t launch_select(const Geometry& g, const int32_t* cu, const int32_t* boff,
-                         const void* q, const float* q_scale, const float* k_mean,
-                         const float* scores, float alpha, int n_sink, int n_local,
-                         uint32_t* keep_bits, int32_t* counts, int32_t* row_ptr,
+hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
+                         const float* k_mean, const float* scores, float alpha, int n_sink,
+                         int n_local, uint32_t* keep_bits, int32_t* counts, int32_t* row_ptr,
                          int32_t* col_idx, hipStream_t st);
 
-hipError_t launch_attn_prep(const Geometry& g, const int32_t* cu, int32_t* boff,
-                            const float* k_mean, const float* v_mean, u16* km16, u16* vm16,
-                            hipStream_t st);
+// Block offsets of the map plus bf16 copies of the pooled keys / values.
+hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_mean,
+                            const float* v_mean, u16* km16, u16* vm16, hipStream_t st);
 
-hipError_t launch_attn(const Geometry& g, const int32_t* cu, const int32_t* boff,
-                       const int32_t* page_table, const void* q, const void* k_cache,
-                       const void* v_cache, const float* q_scale, const float* k_scale,
-                       const int32_t* row_ptr, const int32_t* col_idx, const u16* km16,
-                       const u16* vm16, int correction, void* out, float* lse, hipStream_t st);
+hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_table, const void* q,
+                       const void* k_cache, const void* v_cache, const float* q_scale,
+                       const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
+                       const u16* km16, const u16* vm16, int correction, void* out, float* lse,
+                       hipStream_t st);
 
 }  // namespace fp

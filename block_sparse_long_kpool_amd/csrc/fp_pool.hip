@@ -6,37 +6,11 @@
 
 namespace fp {
 
-// One workgroup: boff[s] = sum_{s' < s} ceil(len_s' / 128), chunked scan.
-__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int num_seqs,
-                                                   int32_t* __restrict__ boff) {
-  __shared__ int buf[256];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < num_seqs; base += 256) {
-    int s = base + (int)threadIdx.x;
-    int n = 0;
-    if (s < num_seqs) n = (cu[s + 1] - cu[s] + kBlock - 1) / kBlock;
-    buf[threadIdx.x] = n;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      int v = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
-      __syncthreads();
-      buf[threadIdx.x] += v;
-      __syncthreads();
-    }
-    int incl = buf[threadIdx.x];
-    int c = carry;
-    if (s < num_seqs) boff[s] = c + incl - n;
-    __syncthreads();
-    if (threadIdx.x == 255) carry = c + incl;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) boff[num_seqs] = carry;
-}
+// One workgroup: kboff / qboff of the sequence map (chunked scans).
+__global__ __launch_bounds__(256) void plan_kernel(SeqMap m) { plan_offsets(m); }
 
-hipError_t launch_plan(const int32_t* cu, int num_seqs, int32_t* boff, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, cu, num_seqs, boff);
+hipError_t launch_plan(const SeqMap& m, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 
@@ -66,12 +40,12 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) 
   }
 }
 
-// grid (N blocks, Hkv, 2 = {K, V}); 256 threads = 16 token lanes x 16 chunks
-// of 8 head-dim elements.  Summation order is fixed (deterministic).
+// grid (NK key blocks, Hkv, 2 = {K, V}); 256 threads = 16 token lanes x 16
+// chunks of 8 head-dim elements.  Every key block of the cache is pooled,
+// cached prefix included.  Summation order is fixed (deterministic).
 template <int KDT, int VDT>
 __global__ __launch_bounds__(256) void pool_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ boff, int num_seqs,
-    const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
+    SeqMap m, const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
     int64_t num_blocks, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ k_scale, float* __restrict__ k_mean, float* __restrict__ v_mean,
     u16* __restrict__ k_mean_bf16) {
@@ -79,9 +53,9 @@ __global__ __launch_bounds__(256) void pool_kernel(
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z == 1;
-  const int s = find_seq(boff, num_seqs, gb);
-  const int J = gb - boff[s];
-  const int len = cu[s + 1] - cu[s];
+  const int s = find_seq(m.kboff, m.num_seqs, gb);
+  const int J = gb - m.kboff[s];
+  const int len = (m.ctx ? m.ctx[s] : 0) + m.cu[s + 1] - m.cu[s];
   const int p0 = J * kBlock;
   const int nJ = min(kBlock, len - p0);
   const int chunk = threadIdx.x & 15;
@@ -123,14 +97,13 @@ __global__ __launch_bounds__(256) void pool_kernel(
   }
 }
 
-hipError_t launch_pool(const Geometry& g, const int32_t* cu, const int32_t* boff,
-                       const int32_t* page_table, const void* k_cache, const void* v_cache,
-                       const float* k_scale, float* k_mean, float* v_mean, u16* k_mean_bf16,
-                       hipStream_t st) {
+hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
+                       const void* k_cache, const void* v_cache, const float* k_scale,
+                       float* k_mean, float* v_mean, u16* k_mean_bf16, hipStream_t st) {
   dim3 grid((unsigned)g.num_blocks, (unsigned)g.hkv, 2);
 #define FP_POOL(KD, VD)                                                                       \
-  hipLaunchKernelGGL((pool_kernel<KD, VD>), grid, dim3(256), 0, st, cu, boff, g.num_seqs,     \
-                     page_table, g.max_pages, g.page_size, g.hkv, g.num_blocks, k_cache,      \
+  hipLaunchKernelGGL((pool_kernel<KD, VD>), grid, dim3(256), 0, st, m, page_table,            \
+                     g.max_pages, g.page_size, g.hkv, g.num_blocks, k_cache,                   \
                      v_cache, k_scale, k_mean, v_mean, k_mean_bf16)
   if (g.qk_dtype == FP_BF16 && g.v_dtype == FP_BF16) FP_POOL(FP_BF16, FP_BF16);
   else if (g.qk_dtype == FP_E4M3 && g.v_dtype == FP_BF16) FP_POOL(FP_E4M3, FP_BF16);

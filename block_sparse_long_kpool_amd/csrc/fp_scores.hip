@@ -49,14 +49,14 @@ struct ScoresSmem {
 constexpr size_t kScoresSmem = sizeof(ScoresSmem);
 
 struct ScoresArgs {
-  const int32_t* cu;
-  const int32_t* boff;
+  SeqMap m;
   const void* q;
   const float* q_scale;
   const u16* kmean16;
   float* scores;
-  int64_t num_blocks;
-  int num_seqs, hq, hkv, group, max_blocks;
+  int64_t num_blocks;   // NK (pooled rows per KV head)
+  int64_t num_qblocks;  // NQ (score rows per KV head)
+  int hq, hkv, group, max_blocks;
   float logit_scale;
 };
 
@@ -195,18 +195,17 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // heaviest rows (largest I) first
-  const int64_t item = (int64_t)a.hkv * a.num_blocks - 1 - blockIdx.x;
+  // heaviest rows (largest I of a sequence) first
+  const int64_t item = (int64_t)a.hkv * a.num_qblocks - 1 - blockIdx.x;
   const int h = (int)(item % a.hkv);
-  const int gb = (int)(item / a.hkv);
-  const int s = find_seq(a.boff, a.num_seqs, gb);
-  const int I = gb - a.boff[s];
-  const int len = a.cu[s + 1] - a.cu[s];
-  const int nI = min(kBlock, len - I * kBlock);
-  const int64_t tok0 = (int64_t)a.cu[s] + (int64_t)I * kBlock;
-  const u16* kbase = a.kmean16 + ((int64_t)h * a.num_blocks + a.boff[s]) * kHeadDim;
+  const int gq = (int)(item / a.hkv);
+  const QBlock qb = query_block(a.m, gq);
+  const int I = qb.I;
+  const int nI = qb.nI;
+  const int64_t tok0 = qb.tok0;
+  const u16* kbase = a.kmean16 + ((int64_t)h * a.num_blocks + qb.kb0) * kHeadDim;
   const int64_t lo_off = (int64_t)a.hkv * a.num_blocks * kHeadDim;  // lo part follows the hi part
-  float* out_row = a.scores + ((int64_t)h * a.num_blocks + gb) * a.max_blocks;
+  float* out_row = a.scores + ((int64_t)h * a.num_qblocks + gq) * a.max_blocks;
   const int ncols = I + 1;
   const int ntiles = (ncols + kJT - 1) / kJT;
   const int nchunks = 4 * a.group;  // 32-row chunks: (head, 32-token slice)
@@ -313,19 +312,17 @@ hipError_t launch_scores_t(const ScoresArgs& a, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_scores(const Geometry& g, const int32_t* cu, const int32_t* boff, const void* q,
-                         const float* q_scale, const u16* k_mean_bf16, float* scores,
-                         hipStream_t st) {
-  const dim3 grid((unsigned)(g.hkv * g.num_blocks));
+hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
+                         const u16* k_mean_bf16, float* scores, hipStream_t st) {
+  const dim3 grid((unsigned)(g.hkv * g.num_qblocks));
   ScoresArgs a;
-  a.cu = cu;
-  a.boff = boff;
+  a.m = m;
   a.q = q;
   a.q_scale = q_scale;
   a.kmean16 = k_mean_bf16;
   a.scores = scores;
   a.num_blocks = g.num_blocks;
-  a.num_seqs = g.num_seqs;
+  a.num_qblocks = g.num_qblocks;
   a.hq = g.hq;
   a.hkv = g.hkv;
   a.group = g.group;

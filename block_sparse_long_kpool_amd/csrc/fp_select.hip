@@ -174,8 +174,8 @@ __device__ double exact_score_wg(const void* q, const float* q_scale, const floa
 // of the row's bitmask and the count.
 template <int QDT>
 __global__ __launch_bounds__(kSelThreads) void decide_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ boff, int num_seqs, int hq,
-    int hkv, int group, int64_t num_blocks, int max_blocks, float softmax_scale,
+    SeqMap m, int hq, int hkv, int group, int64_t num_blocks, int64_t num_qblocks,
+    int max_blocks, float softmax_scale,
     const void* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ k_mean, const float* __restrict__ scores, float alpha, int n_sink,
     int n_local, uint32_t* __restrict__ keep_bits, int32_t* __restrict__ counts) {
@@ -188,10 +188,9 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t row = blockIdx.x;
-  const int h = (int)(row / num_blocks);
-  const int gb = (int)(row % num_blocks);
-  const int s = find_seq(boff, num_seqs, gb);
-  const int I = gb - boff[s];
+  const int h = (int)(row / num_qblocks);
+  const QBlock qb = query_block(m, (int)(row % num_qblocks));
+  const int I = qb.I;
   const int words = (max_blocks + 31) >> 5;
   uint32_t* bits = keep_bits + row * words;
   const float* L = scores + row * max_blocks;
@@ -251,10 +250,9 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
 
   // pass 2: exact evaluation (uniform loops over the candidate bitmaps)
   if (need) {
-    const int len = cu[s + 1] - cu[s];
-    const int nI = min(kBlock, len - I * kBlock);
-    const int64_t tok0 = (int64_t)cu[s] + (int64_t)I * kBlock;
-    const float* kb = k_mean + ((int64_t)h * num_blocks + boff[s]) * kHeadDim;
+    const int nI = qb.nI;
+    const int64_t tok0 = qb.tok0;
+    const float* kb = k_mean + ((int64_t)h * num_blocks + qb.kb0) * kHeadDim;
     const double ref = (double)lmax;
     double emax = -INFINITY;
     for (int w = 0; w < nw_row; ++w) {
@@ -367,14 +365,14 @@ __global__ __launch_bounds__(256) void compact_kernel(int64_t nrows, int max_blo
 
 }  // namespace
 
-hipError_t launch_select(const Geometry& g, const int32_t* cu, const int32_t* boff, const void* q,
-                         const float* q_scale, const float* k_mean, const float* scores,
-                         float alpha, int n_sink, int n_local, uint32_t* keep_bits,
-                         int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
+hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
+                         const float* k_mean, const float* scores, float alpha, int n_sink,
+                         int n_local, uint32_t* keep_bits, int32_t* counts, int32_t* row_ptr,
+                         int32_t* col_idx, hipStream_t st) {
   const unsigned nwg = (unsigned)g.num_rows;
 #define FP_DEC(QD)                                                                              \
-  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, cu, boff, g.num_seqs,     \
-                     g.hq, g.hkv, g.group, g.num_blocks, g.max_blocks, g.softmax_scale, q,        \
+  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, m, g.hq, g.hkv,  \
+                     g.group, g.num_blocks, g.num_qblocks, g.max_blocks, g.softmax_scale, q,   \
                      q_scale, k_mean, scores, alpha, n_sink, n_local, keep_bits, counts)
   if (g.qk_dtype == FP_BF16) FP_DEC(FP_BF16);
   else if (g.qk_dtype == FP_E4M3) FP_DEC(FP_E4M3);

@@ -31,6 +31,7 @@ class DeviceBatch:
     num_q_heads: int
     num_kv_heads: int
     page_size: int
+    ctx_lens: Optional[list] = None  # cached prefix per sequence (chunked prefill)
 
 
 def upload(batch, device="cuda", out_dtype: Optional[str] = None) -> DeviceBatch:
@@ -57,7 +58,9 @@ def upload(batch, device="cuda", out_dtype: Optional[str] = None) -> DeviceBatch
         cu_host=[int(x) for x in batch.cu_seqlens], qk_dtype=spec.qk_dtype,
         v_dtype=spec.v_dtype, out_dtype=out_dtype or spec.out_dtype,
         num_q_heads=int(batch.q.shape[1]), num_kv_heads=int(batch.k_cache.shape[2]),
-        page_size=int(batch.k_cache.shape[1]))
+        page_size=int(batch.k_cache.shape[1]),
+        ctx_lens=None if getattr(batch, "ctx_lens", None) is None
+        else [int(x) for x in batch.ctx_lens])
 
 
 class Pipeline:
@@ -70,13 +73,15 @@ class Pipeline:
         self.problem = Problem(db.cu_host, db.num_q_heads, db.num_kv_heads, db.page_table,
                                db.page_size, int(db.k_cache.shape[0]), db.qk_dtype, db.v_dtype,
                                db.out_dtype, cu_seqlens_dev=db.cu_seqlens, q_scale=db.q_scale,
-                               k_scale=db.k_scale, softmax_scale=softmax_scale)
+                               k_scale=db.k_scale, softmax_scale=softmax_scale,
+                               ctx_lens=db.ctx_lens)
         p = self.problem
-        N, hkv, T, hq = p.num_blocks, db.num_kv_heads, p.total_tokens, db.num_q_heads
+        N, NQ = p.num_blocks, p.num_query_blocks
+        hkv, T, hq = db.num_kv_heads, p.total_tokens, db.num_q_heads
         f32 = torch.float32
         self.k_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
         self.v_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
-        self.scores = torch.empty((hkv, N, p.max_blocks), dtype=f32, device=dev)
+        self.scores = torch.empty((hkv, NQ, p.max_blocks), dtype=f32, device=dev)
         self.row_ptr = torch.empty(p.num_rows + 1, dtype=torch.int32, device=dev)
         self.col_idx = torch.empty(p.csr_capacity, dtype=torch.int32, device=dev)
         odt = torch.float32 if db.out_dtype == "f32" else torch.bfloat16

@@ -27,9 +27,19 @@
  *     (thread-local).  Faults inside kernels (e.g. an out-of-range page id)
  *     surface at the caller's next synchronisation.
  *   - Results are deterministic: identical inputs give bit-identical outputs.
- *   - Shapes: head_dim = 128 and block_size = 128.  T = cu_seqlens[num_seqs]
- *     tokens, n_s = ceil(len_s / 128) blocks in sequence s, N = sum_s n_s,
- *     n_max = max_s n_s.
+ *   - Shapes: head_dim = 128 and block_size = 128.  Sequence s has
+ *     q_s = cu_seqlens[s+1] - cu_seqlens[s] query tokens, the positions
+ *     c_s .. c_s + q_s - 1 of the sequence, where c_s = ctx_lens[s] is the
+ *     number of tokens already in the KV cache before them (0 when ctx_lens
+ *     is NULL: a whole prompt; else a multiple of 128: chunked prefill, where
+ *     each chunk redoes the block selection for its own query blocks against
+ *     all cached keys; "長文本推理越來越長但你的顯卡等不起…FlashPrefill V2",
+ *     chunked-prefill (分塊預填充) passage).  Its KV cache holds
+ *     len_s = c_s + q_s tokens: nk_s = ceil(len_s / 128) key blocks and
+ *     nq_s = nk_s - c_s / 128 query blocks (I = c_s/128 .. nk_s - 1).
+ *     T = cu_seqlens[num_seqs] query tokens, N = sum_s nk_s key blocks,
+ *     NQ = sum_s nq_s query blocks, n_max = max_s nk_s.  Without ctx_lens,
+ *     NQ = N.
  *   - Layouts (row-major, innermost last):
  *       q          [T, Hq, 128]                      dtype qk_dtype
  *       k_cache    [num_pages, page_size, Hkv, 128]  dtype qk_dtype
@@ -38,10 +48,13 @@
  *                  s lives at page page_table[s][p / page_size], slot
  *                  p % page_size (FlashPrefill V2 article, paged KV section:
  *                  page base from the table plus in-page offset).
- *       k_mean, v_mean [Hkv, N, 128] float32 (block b of sequence s at row
- *                  boff_s + b, boff_s = sum of n over earlier sequences)
- *       block_scores   [Hkv, N, n_max] float32
- *       row_ptr    [Hkv * N + 1] int32, rows ordered (kv head, sequence,
+ *       k_mean, v_mean [Hkv, N, 128] float32 (key block J of sequence s at
+ *                  row kboff_s + J, kboff_s = sum of nk over earlier
+ *                  sequences)
+ *       block_scores   [Hkv, NQ, n_max] float32 (query block I of sequence s
+ *                  at row qboff_s + I - c_s/128, qboff_s = sum of nq over
+ *                  earlier sequences; entry J for J <= I)
+ *       row_ptr    [Hkv * NQ + 1] int32, rows ordered (kv head, sequence,
  *                  query block); col_idx int32 block indices inside the
  *                  sequence, ascending per row.
  *       out        [T, Hq, 128] dtype out_dtype
@@ -100,18 +113,22 @@ typedef struct {
   const float* q_scale_dev;        /* DEVICE [Hq]  (qk_dtype == FP_E4M3), else NULL   */
   const float* k_scale_dev;        /* DEVICE [Hkv] (qk_dtype == FP_E4M3), else NULL   */
   float softmax_scale;             /* logit scale; <= 0 selects 1/sqrt(head_dim)      */
+  const int32_t* ctx_lens_host;    /* HOST   [num_seqs] cached prefix per sequence, a
+                                      multiple of 128, or NULL for none             */
+  const int32_t* ctx_lens_dev;     /* DEVICE [num_seqs], same values (NULL iff host is) */
 } fp_problem;
 
 /* Supported dtype combinations (qk, v): (F32, F32), (BF16, BF16), (E4M3, BF16);
  * out_dtype F32 or BF16 with any of them.  Longest sequence <= 8192 blocks. */
 
-/* ---- size queries (host only, read cu_seqlens_host) -------------------- */
-int64_t fp_num_blocks(const fp_problem* p);     /* N = sum_s n_s            */
-int32_t fp_max_blocks(const fp_problem* p);     /* n_max                    */
-int64_t fp_num_rows(const fp_problem* p);       /* Hkv * N (CSR rows)       */
-int64_t fp_scores_elems(const fp_problem* p);   /* Hkv * N * n_max          */
-int64_t fp_csr_capacity(const fp_problem* p);   /* Hkv * sum_s n_s (n_s + 1) / 2,
-                                                   every causal block kept   */
+/* ---- size queries (host only, read cu_seqlens_host / ctx_lens_host) ---- */
+int64_t fp_num_blocks(const fp_problem* p);       /* N = sum_s nk_s (pooled rows) */
+int64_t fp_num_query_blocks(const fp_problem* p); /* NQ = sum_s nq_s              */
+int32_t fp_max_blocks(const fp_problem* p);       /* n_max                        */
+int64_t fp_num_rows(const fp_problem* p);         /* Hkv * NQ (CSR rows)          */
+int64_t fp_scores_elems(const fp_problem* p);     /* Hkv * NQ * n_max             */
+int64_t fp_csr_capacity(const fp_problem* p);     /* Hkv * sum over query blocks of
+                                                     (I + 1): every causal block kept */
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which);
 const char* fp_status_string(int32_t status);
 const char* fp_last_error(void);
@@ -120,22 +137,24 @@ const char* fp_last_error(void);
  * fp_discover -- block pooling and pooled block scores.
  *
  * Pooling (FlashPrefill summary "长上下文加速 28 倍", 3.1 key pooling; V2 paper
- * reading 4.1): k_mean[h][boff_s + J] = mean of the keys of block J of
+ * reading 4.1): k_mean[h][kboff_s + J] = mean of the keys of block J of
  * sequence s for KV head h (n_J = tokens actually in the block); v_mean the
  * same for values.
  *
  * Scores (same summary, 3.1 query pooling + global re-weighting): for KV head
- * h and query block I, let rows(I) be every (query head of h's group, token
- * of block I) and x_rJ = softmax_scale * q_r . kbar_J for J <= I.  Then
- *     block_scores[h][boff_s + I][J] = M_IJ + ln S_IJ,
+ * h and query block I, let rows(I) be every (query head of h's group, query
+ * token of block I) and x_rJ = softmax_scale * q_r . kbar_J for J <= I (key
+ * blocks of the cached prefix included).  Then
+ *     block_scores[h][qboff_s + I - c_s/128][J] = M_IJ + ln S_IJ,
  *     M_IJ = max_r x_rJ,  S_IJ = sum_r exp(x_rJ - M_IJ),
  * the log of the max-normalised exp-sum.  Re-weighting a row against its top
  * block is a subtraction of max_J of this value (done by fp_select).
  * Entries with J > I are left unspecified.
  *
- * The dot products run on bf16 MFMA with kbar rounded to bf16; the result
- * therefore carries an absolute error of a few 1e-3 (natural-log units),
- * which fp_select accounts for.
+ * The dot products run on bf16 MFMA with kbar split into two bf16 terms
+ * (hi + lo, fp32 accumulation); the result carries an absolute error of a
+ * few 1e-5 (natural-log units) on attention-scale logits, which fp_select
+ * accounts for.
  *
  * q, k_cache, v_cache: inputs (layouts above).  k_mean, v_mean, block_scores:
  * outputs.  ws: FP_WS_DISCOVER workspace.
@@ -157,7 +176,7 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache,
  * Kept indices are written ascending (compaction, same summary 3.3).
  *
  * Because block_scores comes from a bf16 fast path, every entry whose fast
- * value lies within 0.05 (natural-log units) of the threshold, together
+ * value lies within 2e-3 (natural-log units) of the threshold, together
  * with the row's candidates for the maximum, is re-evaluated from q and
  * k_mean in float64 before it is decided; all other decisions have a margin
  * far larger than the fast path's error.
@@ -175,7 +194,8 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
  * fp_sparse_attn_paged -- sparse causal attention over the listed blocks with
  * block-mean correction.
  *
- * For query head hq, token at position p of block I of sequence s, and the
+ * For query head hq, query token at position p (counted from the start of
+ * the sequence, cached prefix included) of block I of sequence s, and the
  * list K(h, s, I) = col_idx[row_ptr[r] .. row_ptr[r+1]) of row r = (h, s, I):
  *   E = { tokens j <= p of the listed blocks },  y_j = softmax_scale * q . k_j
  *   C = { J <= I not listed } if mean_correction, else empty,
@@ -184,7 +204,7 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
  *   lse = ln(sum_E e^{y_j} + sum_C e^{z_J})
  * (V2 paper reading 4.1: each pruned block contributes n_J e^{q.kbar} vbar to
  * the numerator and n_J e^{q.kbar} to the denominator.)  Every list must
- * contain its diagonal block I; listed blocks must be < n_s, ascending.
+ * contain its diagonal block I; listed blocks must be <= I, ascending.
  *
  * The g = Hq / Hkv query heads of a KV head are packed into shared K/V tiles
  * (PackGQA, V2 paper reading 4.2(1)); K/V tiles are gathered through the page

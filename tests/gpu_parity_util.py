@@ -56,8 +56,7 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
     default all).  Returns a stats dict; raises AssertionError on failure."""
     prob = OracleProblem.from_workload(w)
     spec = w.spec
-    boff = prob.block_offsets()
-    nblk = int(boff[-1])
+    qoff = prob.query_block_offsets()
     t0 = time.time()
     if check_pool:
         km, vm, _ = pooled_all(prob)
@@ -71,9 +70,10 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
     stats = dict(rows=len(res), band=0, mismatch=0, score_err=0.0, out_err=0.0, lse_err=0.0)
     G = spec.group
     for (h, s, I), r in res.items():
-        row = h * nblk + int(boff[s]) + I
+        row = prob.row_index(h, s, I)
+        i0 = prob.ctx(s) // spec.block_size
         # pooled scores (fast path)
-        Lg = g["scores"][h, int(boff[s]) + I, :I + 1].astype(np.float64)
+        Lg = g["scores"][h, int(qoff[s]) + I - i0, :I + 1].astype(np.float64)
         serr = float(np.max(np.abs(Lg - r["L"])))
         stats["score_err"] = max(stats["score_err"], serr)
         # CSR: exact outside the band
@@ -87,7 +87,7 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
         # outputs
         cu0 = int(w.cu_seqlens[s])
         nI = r["out"].shape[1]
-        toks = cu0 + I * spec.block_size + np.arange(nI)
+        toks = cu0 + I * spec.block_size - prob.ctx(s) + np.arange(nI)
         og = g["out"][toks][:, h * G:(h + 1) * G, :].transpose(1, 0, 2)
         stats["out_err"] = max(stats["out_err"], float(np.max(np.abs(og - r["out"]))))
         lg = g["lse"][h * G:(h + 1) * G][:, toks]
@@ -103,14 +103,16 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
 
 def sample_rows(w, n_per_head, seed=0):
     """Seeded sample of (h, s, I) rows, always including each sequence's
-    first and last block."""
+    first and last query block."""
     rng = np.random.default_rng(seed)
-    spec = w.spec
+    prob = OracleProblem.from_workload(w)
     rows = []
-    for s, L in enumerate(spec.seqlens):
-        n = -(-L // spec.block_size)
-        for h in range(spec.num_kv_heads):
-            pick = set([0, n - 1])
-            pick |= set(int(x) for x in rng.choice(n, size=min(n, n_per_head), replace=False))
+    for s in range(prob.num_seqs):
+        qb = list(prob.query_blocks(s))
+        if not qb:
+            continue
+        for h in range(prob.hkv):
+            pick = set([qb[0], qb[-1]])
+            pick |= set(int(x) for x in rng.choice(qb, size=min(len(qb), n_per_head), replace=False))
             rows += [(h, s, I) for I in sorted(pick)]
     return rows

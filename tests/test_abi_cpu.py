@@ -46,7 +46,8 @@ def _problem(bind, seqlens=(300, 129, 1), hq=8, hkv=2, page=16, qk="bf16", v="bf
              out="bf16", **kw):
     import torch
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
-    maxp = max(1, -(-max(seqlens) // page))
+    ctx = kw.get("ctx_lens") or [0] * len(seqlens)
+    maxp = max(1, -(-max(a + max(b, 0) for a, b in zip(seqlens, ctx)) // page))
     table = torch.zeros((len(seqlens), maxp), dtype=torch.int32)
     return bind.Problem(cu.tolist(), hq, hkv, table, page, 1000, qk, v, out,
                         cu_seqlens_dev=torch.from_numpy(cu), **kw)
@@ -96,3 +97,28 @@ def test_null_pointers_and_small_workspace_are_rejected(bind):
     assert lib.fp_sparse_attn_paged(p.ref, 1, 1, 1, 1, 1, None, None, 1, 1, None, 256,
                                     1 << 30, None) == -1
     assert lib.fp_status_string(-3) == b"workspace too small"
+
+
+def test_size_queries_chunked_prefill(bind):
+    """Cached prefixes (chunked prefill): key blocks cover prefix + chunk,
+    rows cover the chunk's query blocks only."""
+    ctx = [256, 0, 512, 128]
+    p = _problem(bind, seqlens=(300, 129, 0, 1000), ctx_lens=ctx)
+    nk = [5, 2, 4, 9]          # ceil((ctx + q) / 128)
+    i0 = [2, 0, 4, 1]          # first query block
+    nq = [a - b for a, b in zip(nk, i0)]
+    assert p.num_blocks == sum(nk)
+    assert p.num_query_blocks == sum(nq)
+    assert p.max_blocks == 9
+    assert p.num_rows == 2 * sum(nq)
+    assert p.scores_elems == 2 * sum(nq) * 9
+    assert p.csr_capacity == 2 * sum(a * (a + 1) // 2 - b * (b + 1) // 2 for a, b in zip(nk, i0))
+
+
+@pytest.mark.parametrize("ctx", [[100, 0, 0], [-128, 0, 0]])
+def test_invalid_prefix_lengths_are_rejected(bind, ctx):
+    p = _problem(bind, ctx_lens=ctx)
+    with pytest.raises(bind.FpError):
+        _ = p.num_blocks
+    lib = bind.load_library()
+    assert lib.fp_discover(p.ref, 1, 1, 1, 1, 1, 1, 256, 1 << 20, None) == -1

@@ -6,7 +6,7 @@ within max-abs 2e-2 (bf16 / fp32 inputs) or 6e-2 (fp8 e4m3 Q/K)."""
 import numpy as np
 import pytest
 
-from synthetic import custom_spec, make_workload, spec_for
+from synthetic import chunk_view, custom_spec, make_workload, spec_for
 
 from gpu_parity_util import compare, log, run_gpu, sample_rows
 
@@ -135,3 +135,69 @@ def test_max_blocks_per_sequence():
         assert lst[-1] == I and np.all(np.diff(lst) > 0) and lst[0] >= 0
         assert set(range(min(2, I + 1))) <= set(lst.tolist())
         assert set(range(max(0, I - 3), I + 1)) <= set(lst.tolist())
+
+
+CHUNK_CASES = [
+    # name, spec kwargs, cached prefix per sequence
+    ("chunk_bf16_mixed", dict(seqlens=(700, 300, 1000), num_q_heads=8, num_kv_heads=2,
+                              page_size=16, paging="permute", seed=140), (256, 0, 896)),
+    ("chunk_e4m3_tail", dict(seqlens=(1300, 500), num_q_heads=8, num_kv_heads=1, qk_dtype="e4m3",
+                             v_dtype="bf16", page_size=64, paging="roundrobin", seed=141), (1280, 384)),
+    ("chunk_prefix_only", dict(seqlens=(640, 257), num_q_heads=4, num_kv_heads=4, page_size=256,
+                               seed=142), (640, 128)),
+]
+
+
+@pytest.mark.parametrize("name,kw,ctx", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_chunked_prefill_parity(name, kw, ctx):
+    """Chunked prefill: the query tokens follow a cached prefix of each
+    sequence (a sequence may have no query tokens left)."""
+    log(f"case {name}")
+    w = chunk_view(make_workload(custom_spec(name=name, **kw)), ctx)
+    g = run_gpu(w, 0.1)
+    compare(w, g, 0.1)
+
+
+def _chunk_vs_whole(w, ctx, alpha=0.1):
+    """GPU rows of the chunk must be bit-identical to the same rows of the
+    whole prompt: pooled means, scores, lists, outputs and lse."""
+    from oracle import OracleProblem
+    wc = chunk_view(w, ctx)
+    gf = run_gpu(w, alpha)
+    gc = run_gpu(wc, alpha)
+    pf, pc = OracleProblem.from_workload(w), OracleProblem.from_workload(wc)
+    assert np.array_equal(gf["k_mean"], gc["k_mean"]) and np.array_equal(gf["v_mean"], gc["v_mean"])
+    G = w.spec.group
+    for s in range(pc.num_seqs):
+        i0 = ctx[s] // 128
+        qf, qc = pf.query_block_offsets(), pc.query_block_offsets()
+        for h in range(pc.hkv):
+            for I in pc.query_blocks(s):
+                a = gf["scores"][h, int(qf[s]) + I, :I + 1]
+                b = gc["scores"][h, int(qc[s]) + I - i0, :I + 1]
+                assert np.array_equal(a, b), (s, h, I)
+                rf, rc = pf.row_index(h, s, I), pc.row_index(h, s, I)
+                assert np.array_equal(gf["col_idx"][gf["row_ptr"][rf]:gf["row_ptr"][rf + 1]],
+                                      gc["col_idx"][gc["row_ptr"][rc]:gc["row_ptr"][rc + 1]]), (s, h, I)
+        tf = np.arange(int(w.cu_seqlens[s]) + ctx[s], int(w.cu_seqlens[s + 1]))
+        tc = np.arange(int(wc.cu_seqlens[s]), int(wc.cu_seqlens[s + 1]))
+        assert np.array_equal(gf["out"][tf], gc["out"][tc]), s
+        assert np.array_equal(gf["lse"][:, tf], gc["lse"][:, tc]), s
+    return wc, gc
+
+
+def test_chunked_prefill_matches_whole_prompt():
+    log("case chunk_vs_whole_small")
+    w = make_workload(custom_spec(name="chunk_whole", seqlens=(1500, 900, 300), num_q_heads=16,
+                                  num_kv_heads=2, page_size=64, paging="permute", seed=143))
+    _chunk_vs_whole(w, (1024, 512, 0))
+
+
+def test_chunked_prefill_128k_last_16k():
+    """The last 16K tokens of the 128K prompt as one chunk (the launch
+    configuration of the chunked benchmark line): bit-identical to the whole
+    prompt's rows; oracle parity on sampled rows of the chunk."""
+    log("case chunk_128k_last16k")
+    w = make_workload(spec_for("sweep_128k"))
+    wc, gc = _chunk_vs_whole(w, (131072 - 16384,))
+    compare(wc, gc, 0.1, rows=sample_rows(wc, 4), check_pool=False)
