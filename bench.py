@@ -125,7 +125,7 @@ def kept_pairs(row_ptr, col_idx, spec, ctx=None):
     return kept * g, corr * g
 
 
-def gpu_setup(spec, threads=None, ctx=None):
+def gpu_setup(spec, threads=None, ctx=None, attn_splits=0):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
     from synthetic import chunk_view, make_workload
@@ -135,7 +135,7 @@ def gpu_setup(spec, threads=None, ctx=None):
         w = chunk_view(w, ctx)
     t_gen = time.time() - t0
     db = upload(w, "cuda")
-    pipe = Pipeline(db)
+    pipe = Pipeline(db, attn_splits=attn_splits)
     torch.cuda.synchronize()
     return w, pipe, t_gen
 
@@ -223,6 +223,8 @@ def main():
                     help="also time the alpha sweep x correction (written to --sweep-out)")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-splits", type=int, default=0,
+                    help="KV split of the attention: 0 automatic, 1 never, n parts per row")
     ap.add_argument("--chunk-ctx", type=int, default=None, metavar="TOKENS",
                     help="chunked prefill: the first TOKENS tokens of every prompt are already "
                          "cached (a multiple of 128); the step processes the rest")
@@ -249,7 +251,7 @@ def main():
     correction = not args.no_correction
     ctx = None if args.chunk_ctx is None else [min(args.chunk_ctx, L) // 128 * 128
                                                for L in spec.seqlens]
-    w, pipe, t_gen = gpu_setup(spec, ctx=ctx)
+    w, pipe, t_gen = gpu_setup(spec, ctx=ctx, attn_splits=args.attn_splits)
     print(f"# generated {spec.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
     t = time_steps(pipe, args.alpha, correction, args.steps, args.warmup)
     rp, ci = pipe.csr()
@@ -313,6 +315,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.attn_splits:
+        line["config"]["attn_splits"] = args.attn_splits
     if ctx is not None:
         line["config"]["chunk"] = {"cached_tokens": ctx, "query_tokens":
                                    [L - c for L, c in zip(spec.seqlens, ctx)]}

@@ -53,6 +53,7 @@ class FpProblemC(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("ctx_lens_host", ctypes.POINTER(ctypes.c_int32)),
         ("ctx_lens_dev", ctypes.c_void_p),
+        ("attn_splits", ctypes.c_int32),
     ]
 
 
@@ -124,7 +125,8 @@ class Problem:
     def __init__(self, cu_seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int,
                  page_table, page_size: int, num_pages: int, qk_dtype: str, v_dtype: str,
                  out_dtype: str, cu_seqlens_dev=None, q_scale=None, k_scale=None,
-                 softmax_scale: float = 0.0, device=None, ctx_lens: Optional[Sequence[int]] = None):
+                 softmax_scale: float = 0.0, device=None, ctx_lens: Optional[Sequence[int]] = None,
+                 attn_splits: int = 0):
         import torch
         self.device = device or page_table.device
         cu = [int(x) for x in cu_seqlens]
@@ -165,6 +167,7 @@ class Problem:
         if self.ctx_host is not None:
             c.ctx_lens_host = self.ctx_host
             c.ctx_lens_dev = _ptr(self.ctx_dev)
+        c.attn_splits = attn_splits
         self.c = c
         self.lib = load_library()
 

@@ -93,12 +93,14 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   g->v_dtype = vd;
   g->out_dtype = od;
   g->softmax_scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  if (p->attn_splits < 0) return fail(FP_ERR_INVALID, "attn_splits must be >= 0 (got %d)", p->attn_splits);
+  g->attn_splits = p->attn_splits;
   return FP_OK;
 }
 
 struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; };
 struct SelectWs { int32_t* kboff; int32_t* qboff; uint32_t* bits; int32_t* counts; };
-struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; };
+struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; float* opart; float* lpart; };
 
 SeqMap seq_map(const fp_problem* p, int32_t* kboff, int32_t* qboff) {
   SeqMap m;
@@ -140,6 +142,13 @@ size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
     w.qboff = (int32_t*)take(boff_bytes);
     w.km16 = (u16*)take(pooled16);
     w.vm16 = (u16*)take(pooled16);
+    w.opart = w.lpart = nullptr;
+    const int splits = attn_splits(g);
+    if (splits > 1) {  // partial outputs and lse of the KV-split parts
+      const size_t rows = (size_t)splits * (size_t)g.total_tokens * (size_t)g.hq;
+      w.opart = (float*)take(sizeof(float) * rows * kHeadDim);
+      w.lpart = (float*)take(sizeof(float) * rows);
+    }
     if (out) *reinterpret_cast<AttnWs*>(out) = w;
   } else {
     return 0;
@@ -293,7 +302,7 @@ int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache
     return st;
   return hip_status(launch_attn(g, m, p->page_table_dev, q, k_cache, v_cache, p->q_scale_dev,
                                 p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
-                                mean_correction ? 1 : 0, out, lse, s),
+                                mean_correction ? 1 : 0, out, lse, w.opart, w.lpart, s),
                     "attn");
 }
 

@@ -30,6 +30,7 @@
 //     ds_read_b64_tr_b16 (16x4 transposes inside 16-lane groups).
 //   * correction tiles: 128 pooled keys/values (bf16) per tile with a
 //     log2(n_J) bias; listed blocks and J > I are masked to -inf.
+#include <algorithm>
 #include <type_traits>
 
 #include "fp_internal.hpp"
@@ -47,6 +48,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // magnitude.  In practice the rescale then runs at most once per row.
 constexpr float kLazy = 64.0f;
 constexpr float kLazyBound = 18446744073709551616.0f;  // 2^kLazy
+// Initial running max: finite, so that a masked logit (-inf) minus it stays
+// -inf (probability 0) and no inf - inf ever forms; any real logit exceeds it
+// by far more than kLazy, so a row's first chunk always takes the exact path
+// (its sum is +inf).  A row that has seen only masked keys keeps m = kMInit
+// and l = 0.  (A part of a KV-split row may start with a diagonal or a
+// correction tile, whose first chunk can be fully masked for some rows.)
+constexpr float kMInit = -1e30f;
 constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
 #ifndef FP_ATTN_WAVES
 #define FP_ATTN_WAVES 8
@@ -68,6 +76,9 @@ struct AttnArgs {
   const u16* vm16;
   void* out;
   float* lse;
+  float* opart;  // splits > 1: [splits, T, Hq, d] partial outputs (each normalised by its own sum)
+  float* lpart;  // splits > 1: [splits, Hq, T] partial lse (natural log; -inf for an empty part)
+  int splits;    // workgroups per (row, head pack), each over a contiguous part of the tile list
   int64_t num_blocks;   // NK (pooled rows per KV head)
   int64_t num_qblocks;  // NQ (CSR rows per KV head)
   int64_t total_tokens;
@@ -128,7 +139,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int xcd = b & 7;
   const int kq = b >> 3;
   const int pack = kq % a.packs;
-  const int64_t row_ord = (int64_t)(kq / a.packs) * 8 + xcd;
+  const int split = (kq / a.packs) % a.splits;
+  const int64_t row_ord = (int64_t)(kq / a.packs / a.splits) * 8 + xcd;
   const int64_t nrows = (int64_t)a.hkv * a.num_qblocks;
   if (row_ord >= nrows) return;
   const int h = (int)(row_ord % a.hkv);
@@ -237,6 +249,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   }
   const int npooled = a.correction ? sm.npooled : 0;
   const int ntiles = nkept + npooled;
+  // KV split: this workgroup takes tiles [tbeg, tend) of the row's list
+  // (contiguous parts balanced by tile count; all of it without a split)
+  const int tbeg = (int)(((int64_t)split * ntiles) / a.splits);
+  const int tend = (int)(((int64_t)(split + 1) * ntiles) / a.splits);
 
   // ---- tile staging -------------------------------------------------------
   // Kept block J: token rows J*128 .. +127 of the sequence (rows past the end
@@ -255,14 +271,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   auto tile_index = [&](int t) { return (int)sm.tiles[t]; };
   // page id of row `tid` of kept tile t (only threads < 128); -1 if pooled
   auto fetch_page = [&](int t) -> int {
-    if (t >= ntiles || t >= nkept || tid >= kBlock) return -1;
+    if (t >= tend || t >= nkept || tid >= kBlock) return -1;
     const int J = tile_index(t);
     const int p0 = J * kBlock + tid;
     const int p = p0 < len ? p0 : J * kBlock;
     return a.page_table[ptrow + (small_pages ? (p >> pshift) : (p / psz))];
   };
   auto publish_slot = [&](int t, int page, int sbuf) {
-    if (t >= ntiles || t >= nkept || tid >= kBlock) return;
+    if (t >= tend || t >= nkept || tid >= kBlock) return;
     const int J = tile_index(t);
     const int p0 = J * kBlock + tid;
     const int p = p0 < len ? p0 : J * kBlock;
@@ -366,21 +382,21 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   float m_run[RC], l_run[RC];
 #pragma unroll
   for (int rc = 0; rc < RC; ++rc) {
-    m_run[rc] = -INFINITY;
+    m_run[rc] = kMInit;
     l_run[rc] = 0.f;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) o[rc][dc] = f32x16{};
   }
 
-  // prologue: slots of tiles 0 and 1, gathers of tile 0
+  // prologue: slots of the first two tiles, gathers of the first
   {
-    const int page0 = fetch_page(0);  // both page lookups in flight together
-    const int page1 = fetch_page(1);
-    publish_slot(0, page0, 0);
-    publish_slot(1, page1, 1);
+    const int page0 = fetch_page(tbeg);  // both page lookups in flight together
+    const int page1 = fetch_page(tbeg + 1);
+    publish_slot(tbeg, page0, tbeg & 1);
+    publish_slot(tbeg + 1, page1, (tbeg + 1) & 1);
   }
   __syncthreads();
-  if (ntiles > 0) issue_tile(0, 0);
+  if (tbeg < tend) issue_tile(tbeg, tbeg & 1);
   wait_vm();
   __syncthreads();
 
@@ -412,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   auto iterate = [&](int t, auto pooled_c, auto diag_c) {
     constexpr bool POOLED_TILE = decltype(pooled_c)::value;
     const int buf = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if (t + 1 < tend) issue_tile(t + 1, buf ^ 1);
     const int page_next = fetch_page(t + 2);  // consumed after the math below
 
     // The 128-key tile runs as four 32-key chunks c in a software pipeline:
@@ -477,7 +493,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     // P^T operand layout and the chunk's row sums.  Fast path: exponentiate
     // against the running max m_run as is.  The max only has to move when a
     // logit exceeds m_run + kLazy, and then that row's chunk sum exceeds
-    // 2^kLazy (a row's first chunk, with m_run = -inf, gives +inf), so the sum
+    // 2^kLazy (a row's first chunk, with m_run = kMInit, gives +inf), so the sum
     // doubles as the overflow test and the fast path computes no max at all.
     // The slow path (rare) raises the max of the affected rows, rescales the
     // output and recomputes the chunk.
@@ -615,8 +631,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   // tiles, then the diagonal tile (causal mask), each in a loop of its own
   const bool last_is_diag = nkept > 0 && tile_index(nkept - 1) == I;
   const int n_off = last_is_diag ? nkept - 1 : nkept;
-  for (int t = 0; t < n_off; ++t) iterate(t, std::false_type{}, std::false_type{});
-  if (last_is_diag) iterate(nkept - 1, std::false_type{}, std::true_type{});
+  for (int t = tbeg; t < min(n_off, tend); ++t) iterate(t, std::false_type{}, std::false_type{});
+  if (last_is_diag && nkept - 1 >= tbeg && nkept - 1 < tend)
+    iterate(nkept - 1, std::false_type{}, std::true_type{});
   if constexpr (kFp8) {
     // pooled tiles run on bf16 MFMA: widen the fp8 Q fragments (exact)
 #pragma unroll
@@ -630,7 +647,31 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
           qf[rc][kk][i] = f32_to_bf16(e4m3_to_f32(((i < 4 ? wlo : whi) >> (8 * (i & 3))) & 0xFFu));
       }
   }
-  for (int t = nkept; t < ntiles; ++t) iterate(t, std::true_type{}, std::false_type{});
+  for (int t = max(nkept, tbeg); t < tend; ++t) iterate(t, std::true_type{}, std::false_type{});
+
+  if (a.splits > 1) {
+    // part of a split row: O_part = acc / l and lse_part in fp32 for the
+    // combine pass (an empty part: O_part = 0, lse_part = -inf)
+#pragma unroll
+    for (int rc = 0; rc < RC; ++rc) {
+      const float l_tot = l_run[rc] + __shfl_xor(l_run[rc], 32, 64);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (col >= nvalid[rc]) continue;
+      const int64_t tok = tok0 + tbase + 32 * rc + col;
+      float* ob = a.opart + (((int64_t)split * a.total_tokens + tok) * a.hq + hq_idx) * kHeadDim;
+#pragma unroll
+      for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(ob + 32 * dc + 8 * j + 4 * half) =
+              make_float4(o[rc][dc][4 * j] * inv, o[rc][dc][4 * j + 1] * inv,
+                          o[rc][dc][4 * j + 2] * inv, o[rc][dc][4 * j + 3] * inv);
+      if (half == 0)
+        a.lpart[((int64_t)split * a.hq + hq_idx) * a.total_tokens + tok] =
+            l_tot > 0.f ? (m_run[rc] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
 
   // ---- epilogue: O = acc / l, lse = m + log2(l) (natural log out) ----
   if constexpr (kFp8) {
@@ -714,6 +755,42 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   }
 }
 
+// KV-split combine ("長文本推理越來越長但你的顯卡等不起…FlashPrefill V2",
+// KV-split load-balancing passage): the parts of a row, each normalised by
+// its own sum, are merged by their log-sum-exp,
+//   lse = ln sum_s e^{lse_s},  O = sum_s e^{lse_s - lse} O_s.
+// One wave per (token, query head), two head-dim elements per lane.
+template <int ODT>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
+                                                           const float* __restrict__ lpart, int splits,
+                                                           int64_t T, int hq, void* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= T * hq) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = pair / hq;
+  const int hh = (int)(pair % hq);
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, lpart[((int64_t)s * hq + hh) * T + tok]);
+  float tot = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float w = expf(lpart[((int64_t)s * hq + hh) * T + tok] - m);  // empty part: 0
+    const float2 v = *reinterpret_cast<const float2*>(opart + (((int64_t)s * T + tok) * hq + hh) * kHeadDim + 2 * lane);
+    tot += w;
+    o0 = fmaf(w, v.x, o0);
+    o1 = fmaf(w, v.y, o1);
+  }
+  const float inv = 1.f / tot;
+  const int64_t e = (tok * hq + hh) * kHeadDim + 2 * lane;
+  if constexpr (ODT == FP_BF16) {
+    const bf16x2 b = bf16x2{f32_to_bf16(o0 * inv), f32_to_bf16(o1 * inv)};
+    *reinterpret_cast<bf16x2*>(reinterpret_cast<u16*>(out) + e) = b;
+  } else {
+    *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + e) = make_float2(o0 * inv, o1 * inv);
+  }
+  if (lse && lane == 0) lse[(int64_t)hh * T + tok] = m + logf(tot);
+}
+
 // Block offsets of the map (last block of the grid) and bf16 copies of the
 // pooled keys / values.
 __global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const float* __restrict__ km,
@@ -743,11 +820,18 @@ hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_m
   return hipGetLastError();
 }
 
+int attn_splits(const Geometry& g) {
+  if (g.attn_splits > 0) return std::min(g.attn_splits, kAttnMaxSplits);
+  const int64_t wgs = ((g.hkv * g.num_qblocks + 7) / 8) * 8 * ((g.group + 1) / 2);
+  if (2 * wgs > kAttnSplitTarget) return 1;
+  return (int)std::min<int64_t>(kAttnMaxSplits, kAttnSplitTarget / wgs);
+}
+
 hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_table, const void* q,
                        const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                        const u16* km16, const u16* vm16, int correction, void* out, float* lse,
-                       hipStream_t st) {
+                       float* opart, float* lpart, hipStream_t st) {
   AttnArgs a;
   a.m = m;
   a.page_table = page_table;
@@ -762,6 +846,10 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   a.vm16 = vm16;
   a.out = out;
   a.lse = lse;
+  a.splits = attn_splits(g);
+  a.opart = opart;
+  a.lpart = lpart;
+  if (a.splits > 1 && (!opart || !lpart)) return hipErrorInvalidValue;
   a.num_blocks = g.num_blocks;
   a.num_qblocks = g.num_qblocks;
   a.total_tokens = g.total_tokens;
@@ -774,7 +862,7 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   a.correction = correction;
   a.softmax_scale = g.softmax_scale;
   const int64_t rows = (int64_t)g.hkv * g.num_qblocks;
-  const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs);
+  const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs * a.splits);
   const size_t shm = sizeof(SharedMem);
 #define FP_ATTN(QD, VD, OD)                                                                    \
   do {                                                                                         \
@@ -798,6 +886,16 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   else return hipErrorInvalidValue;
 #undef FP_ATTN_O
 #undef FP_ATTN
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  const int64_t pairs = g.total_tokens * g.hq;
+  const unsigned cgrid = (unsigned)((pairs + 3) / 4);
+  if (g.out_dtype == FP_BF16)
+    hipLaunchKernelGGL(attn_combine_kernel<FP_BF16>, dim3(cgrid), dim3(256), 0, st, opart, lpart,
+                       a.splits, g.total_tokens, g.hq, out, lse);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<FP_F32>, dim3(cgrid), dim3(256), 0, st, opart, lpart,
+                       a.splits, g.total_tokens, g.hq, out, lse);
   return hipGetLastError();
 }
 

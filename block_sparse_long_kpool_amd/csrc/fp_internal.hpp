@@ -35,7 +35,16 @@ struct Geometry {
   int64_t total_tokens;  // T (query tokens)
   int qk_dtype, v_dtype, out_dtype;
   float softmax_scale;
+  int attn_splits;  // requested KV split of the attention (0: automatic)
 };
+
+// KV split of the attention: a launch with fewer (row, head-pack) workgroups
+// than kAttnSplitTarget (one per CU) splits each row's tile list into
+// floor(kAttnSplitTarget / workgroups) parts, at most kAttnMaxSplits, merged
+// by a combine pass.  (Measured on 512- and 1K-token chunks after a 127K
+// prefix: more parts than CUs only add partial-output traffic.)
+constexpr int kAttnMaxSplits = 8;
+constexpr int kAttnSplitTarget = 256;
 
 // Where the tokens and blocks of each sequence live (device pointers).  The
 // query tokens cu[s] .. cu[s+1]-1 are the positions ctx[s] .. ctx[s]+qlen-1
@@ -231,10 +240,13 @@ hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, cons
 hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_mean,
                             const float* v_mean, u16* km16, u16* vm16, hipStream_t st);
 
+// Parts per row of the attention launch (1: no split).
+int attn_splits(const Geometry& g);
+
 hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_table, const void* q,
                        const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                        const u16* km16, const u16* vm16, int correction, void* out, float* lse,
-                       hipStream_t st);
+                       float* opart, float* lpart, hipStream_t st);
 
 }  // namespace fp

@@ -66,7 +66,7 @@ def upload(batch, device="cuda", out_dtype: Optional[str] = None) -> DeviceBatch
 class Pipeline:
     """All device buffers of one batch shape, and the three calls in order."""
 
-    def __init__(self, db: DeviceBatch, softmax_scale: float = 0.0):
+    def __init__(self, db: DeviceBatch, softmax_scale: float = 0.0, attn_splits: int = 0):
         import torch
         self.db = db
         dev = db.q.device
@@ -74,7 +74,7 @@ class Pipeline:
                                db.page_size, int(db.k_cache.shape[0]), db.qk_dtype, db.v_dtype,
                                db.out_dtype, cu_seqlens_dev=db.cu_seqlens, q_scale=db.q_scale,
                                k_scale=db.k_scale, softmax_scale=softmax_scale,
-                               ctx_lens=db.ctx_lens)
+                               ctx_lens=db.ctx_lens, attn_splits=attn_splits)
         p = self.problem
         N, NQ = p.num_blocks, p.num_query_blocks
         hkv, T, hq = db.num_kv_heads, p.total_tokens, db.num_q_heads

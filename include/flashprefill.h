@@ -116,6 +116,9 @@ typedef struct {
   const int32_t* ctx_lens_host;    /* HOST   [num_seqs] cached prefix per sequence, a
                                       multiple of 128, or NULL for none             */
   const int32_t* ctx_lens_dev;     /* DEVICE [num_seqs], same values (NULL iff host is) */
+  int32_t attn_splits;             /* KV split of fp_sparse_attn_paged: 0 = automatic,
+                                      1 = never split, n = split every row into n
+                                      parts (at most 8)                              */
 } fp_problem;
 
 /* Supported dtype combinations (qk, v): (F32, F32), (BF16, BF16), (E4M3, BF16);
@@ -212,7 +215,19 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
  * MFMA when qk_dtype == FP_E4M3), PV on bf16 MFMA; softmax in fp32.  Rows
  * are launched last query block first (the work of a row grows with its
  * position: its pooled tiles and, on average, its list), KV heads
- * interleaved, the g/2 workgroups of a row together on one XCD.  A list entry
+ * interleaved, the g/2 workgroups of a row together on one XCD.
+ *
+ * KV split ("長文本推理越來越長但你的顯卡等不起…FlashPrefill V2", KV-split
+ * load-balancing passage: work is divided by the selected blocks, not by
+ * position): when a launch has at most 128 (row, head pair) workgroups
+ * (small chunks) and attn_splits == 0, each row's tile list (listed blocks,
+ * then correction tiles) is cut into floor(256 / workgroups) contiguous parts
+ * (at most 8) with equal tile counts, each part run by its own workgroup,
+ * and a combine pass merges the parts by their log-sum-exp.  The split changes only the rounding of a
+ * row, never which keys it sees; attn_splits = 1 makes a row's result
+ * independent of the rest of the batch (no split ever).  The split count is
+ * a function of the descriptor, so fp_workspace_bytes(FP_WS_ATTN) covers the
+ * partial outputs.  A list entry
  * outside [0, I] or a list longer than I + 1 gives unspecified output for
  * that row but no out-of-bounds access.
  *

@@ -29,11 +29,11 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, alpha, sinks=256, local=512, correction=True):
+def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
     db = upload(w, "cuda")
-    pipe = Pipeline(db)
+    pipe = Pipeline(db, attn_splits=attn_splits)
     pipe.run(alpha, sinks, local, correction)
     torch.cuda.synchronize()
     rp, ci = pipe.csr()
@@ -67,6 +67,10 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
     res = run_pipeline(prob, alpha, sinks, local, correction, rows=rows,
                        given_csr=(g["row_ptr"], g["col_idx"]))
     rp, ci = g["row_ptr"], g["col_idx"]
+    # every output and lse of the batch must be finite (max() below would
+    # silently skip NaN)
+    assert np.all(np.isfinite(g["out"])), "non-finite output"
+    assert np.all(np.isfinite(g["lse"])), "non-finite lse"
     stats = dict(rows=len(res), band=0, mismatch=0, score_err=0.0, out_err=0.0, lse_err=0.0)
     G = spec.group
     for (h, s, I), r in res.items():

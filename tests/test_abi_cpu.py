@@ -122,3 +122,17 @@ def test_invalid_prefix_lengths_are_rejected(bind, ctx):
         _ = p.num_blocks
     lib = bind.load_library()
     assert lib.fp_discover(p.ref, 1, 1, 1, 1, 1, 1, 256, 1 << 20, None) == -1
+
+
+def test_attn_split_workspace_and_validation(bind):
+    """Small launches split the attention automatically; the partial outputs
+    live in the attention workspace.  attn_splits = 1 never splits."""
+    p0 = _problem(bind, seqlens=(300, 129))                  # automatic
+    p1 = _problem(bind, seqlens=(300, 129), attn_splits=1)   # never
+    p4 = _problem(bind, seqlens=(300, 129), attn_splits=4)
+    w0, w1, w4 = (p.workspace_bytes(bind.FP_WS_ATTN) for p in (p0, p1, p4))
+    T, hq = 429, 8
+    assert w4 - w1 >= 4 * T * hq * 129 * 4   # 4 parts x (128 outputs + lse) per (token, head)
+    assert w0 > w1
+    with pytest.raises(bind.FpError):
+        _ = _problem(bind, attn_splits=-1).num_blocks

@@ -46,11 +46,15 @@ SMALL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("splits", [1, 0], ids=["nosplit", "autosplit"])
 @pytest.mark.parametrize("name,kw,alpha,sinks,local,corr", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
-def test_small_full_parity(name, kw, alpha, sinks, local, corr):
-    log(f"case {name}")
+def test_small_full_parity(name, kw, alpha, sinks, local, corr, splits):
+    """Small ragged cases, with the attention unsplit and with the automatic
+    KV split (these launches have far fewer workgroups than CUs, so every
+    row is cut into several parts merged by the combine pass)."""
+    log(f"case {name} splits={splits}")
     w = make_workload(custom_spec(name=name, **kw))
-    g = run_gpu(w, alpha, sinks, local, corr)
+    g = run_gpu(w, alpha, sinks, local, corr, attn_splits=splits)
     compare(w, g, alpha, sinks, local, corr)
 
 
@@ -160,11 +164,13 @@ def test_chunked_prefill_parity(name, kw, ctx):
 
 def _chunk_vs_whole(w, ctx, alpha=0.1):
     """GPU rows of the chunk must be bit-identical to the same rows of the
-    whole prompt: pooled means, scores, lists, outputs and lse."""
+    whole prompt: pooled means, scores, lists, outputs and lse.  The
+    attention runs unsplit on both sides (attn_splits = 1: a row's result
+    then does not depend on the size of the launch)."""
     from oracle import OracleProblem
     wc = chunk_view(w, ctx)
-    gf = run_gpu(w, alpha)
-    gc = run_gpu(wc, alpha)
+    gf = run_gpu(w, alpha, attn_splits=1)
+    gc = run_gpu(wc, alpha, attn_splits=1)
     pf, pc = OracleProblem.from_workload(w), OracleProblem.from_workload(wc)
     assert np.array_equal(gf["k_mean"], gc["k_mean"]) and np.array_equal(gf["v_mean"], gc["v_mean"])
     G = w.spec.group
@@ -201,3 +207,34 @@ def test_chunked_prefill_128k_last_16k():
     w = make_workload(spec_for("sweep_128k"))
     wc, gc = _chunk_vs_whole(w, (131072 - 16384,))
     compare(wc, gc, 0.1, rows=sample_rows(wc, 4), check_pool=False)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 8])
+def test_forced_kv_split_gqa_32k(splits):
+    """32K prompt with every row forced into 2, 3 or 8 parts (parts may be
+    empty for short rows): sampled rows against the oracle, and every output
+    within rounding of the unsplit result."""
+    log(f"case gqa_32k splits={splits}")
+    w = make_workload(spec_for("gqa_32k"))
+    g1 = run_gpu(w, 0.1, attn_splits=1)
+    gs = run_gpu(w, 0.1, attn_splits=splits)
+    assert np.array_equal(g1["col_idx"], gs["col_idx"])
+    dout = np.abs(g1["out"] - gs["out"])
+    dlse = float(np.max(np.abs(g1["lse"] - gs["lse"])))
+    log(f"  split vs unsplit: out {float(dout.max()):.3g} lse {dlse:.3g}")
+    # each part exponentiates against its own running max, so the bf16
+    # probabilities fed to P.V round differently (relative 2^-9 per term);
+    # the log-sum-exp, formed in fp32, agrees to rounding
+    assert np.all(dout <= 2.0 ** -5 * np.maximum(1.0, np.abs(g1["out"])))
+    assert dlse <= 1e-4
+    compare(w, gs, 0.1, rows=sample_rows(w, 3), check_pool=False)
+
+
+def test_small_chunk_auto_split():
+    """A 256-token chunk after an 8K prefix (few rows: the automatic split
+    cuts each row into 8 parts) against the oracle."""
+    log("case chunk_256_after_8k")
+    w = chunk_view(make_workload(custom_spec(name="small_chunk", seqlens=(8448,), num_q_heads=8,
+                                             num_kv_heads=2, page_size=64, seed=150)), (8192,))
+    g = run_gpu(w, 0.1)
+    compare(w, g, 0.1)
