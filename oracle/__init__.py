@@ -19,5 +19,8 @@ from .flashprefill import (  # noqa: F401
     pool_blocks,
     pooled_all,
     run_pipeline,
+    rank_order,
     select_row,
+    select_row_topk,
+    select_row_topp,
 )

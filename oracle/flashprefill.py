@@ -52,6 +52,12 @@ design notes):
   R12 index lists hold block indices inside the sequence, ascending.
   R19 an entry whose Shat lies within 1e-5 * alpha of alpha is "in band":
      both decisions are correct there; such entries are flagged.
+  R21 top-k / top-p selection ([V1] 二: the prior methods sort (top-k) or
+     accumulate probability mass (top-p); 4.4 ablates them against the
+     max-based threshold): ranked by L_IJ (equivalently Score_IJ), ties toward
+     the lower J; top-k adds the k best non-forced blocks to the forced ones;
+     top-p adds the fewest best causal blocks whose share of sum_J e^{L_IJ}
+     reaches p.  Both keep the same sink / local safety net.
   R20 chunked prefill ([V2a] chunked-prefill passage): a chunk's queries are
      positions ctx .. ctx + qlen - 1 of a sequence whose first ctx tokens
      (a multiple of B) are already cached.  Pooling covers every cached key
@@ -316,6 +322,41 @@ def select_row(L_row: np.ndarray, I: int, alpha: float, sink_tokens: int,
     band = (~forced) & (np.abs(Shat - alpha) <= BAND_REL * alpha) if alpha > 0 \
         else np.zeros(I + 1, dtype=bool)
     return np.nonzero(keep)[0].astype(np.int64), band
+
+
+def rank_order(L_row: np.ndarray, I: int) -> np.ndarray:
+    """Causal blocks J <= I by descending score, ties toward the lower J."""
+    L = np.asarray(L_row[:I + 1], dtype=np.float64)
+    return np.array(sorted(range(I + 1), key=lambda J: (-L[J], J)), dtype=np.int64)
+
+
+def select_row_topk(L_row: np.ndarray, I: int, k: int, sink_tokens: int,
+                    local_tokens: int, block_size: int) -> np.ndarray:
+    """Top-k selection, the prior methods' strategy that [V1] 二 and the 4.4
+    ablation compare with the max-based threshold (reading R21): the forced
+    blocks plus the k highest-scoring other causal blocks."""
+    forced = forced_blocks(I, sink_tokens, local_tokens, block_size)
+    ranked = [J for J in rank_order(L_row, I) if not forced[J]]
+    keep = forced.copy()
+    keep[np.asarray(ranked[:max(0, k)], dtype=np.int64)] = True
+    return np.nonzero(keep)[0].astype(np.int64)
+
+
+def select_row_topp(L_row: np.ndarray, I: int, p: float, sink_tokens: int,
+                    local_tokens: int, block_size: int) -> np.ndarray:
+    """Top-p selection ([V1] 二, 4.4; reading R21): the fewest highest-scoring
+    causal blocks whose share of the row's total score sum_J e^{L_IJ} reaches
+    p, plus the forced blocks.  p <= 0 keeps the forced blocks only."""
+    forced = forced_blocks(I, sink_tokens, local_tokens, block_size)
+    keep = forced.copy()
+    if p > 0:
+        L = np.asarray(L_row[:I + 1], dtype=np.float64)
+        order = rank_order(L_row, I)
+        w = np.exp(L[order] - L.max())
+        cum = np.cumsum(w)
+        n = int(np.searchsorted(cum, p * cum[-1], side="left"))  # first cum >= p * total
+        keep[order[:min(n + 1, I + 1)]] = True
+    return np.nonzero(keep)[0].astype(np.int64)
 
 
 # ---------------------------------------------------------------------------
