@@ -27,6 +27,8 @@
 //     accumulator set) are independent of the max / exp / sum of chunk j, so
 //     the matrix core and the VALU overlap; the logit scale is folded into one
 //     fma per element, and masking runs only for the ragged last block.
+#include <algorithm>
+
 #include "fp_internal.hpp"
 
 namespace fp {
@@ -57,6 +59,7 @@ struct ScoresArgs {
   int64_t num_blocks;   // NK (pooled rows per KV head)
   int64_t num_qblocks;  // NQ (score rows per KV head)
   int hq, hkv, group, max_blocks;
+  int cparts;           // workgroups per (kv head, query block), each over a range of key tiles
   float logit_scale;
 };
 
@@ -195,8 +198,10 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // heaviest rows (largest I of a sequence) first
-  const int64_t item = (int64_t)a.hkv * a.num_qblocks - 1 - blockIdx.x;
+  // heaviest rows (largest I of a sequence) first; the cparts workgroups of
+  // a row take contiguous ranges of its key tiles (columns are independent)
+  const int part = (int)(blockIdx.x % a.cparts);
+  const int64_t item = (int64_t)a.hkv * a.num_qblocks - 1 - blockIdx.x / a.cparts;
   const int h = (int)(item % a.hkv);
   const int gq = (int)(item / a.hkv);
   const QBlock qb = query_block(a.m, gq);
@@ -207,7 +212,10 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   const int64_t lo_off = (int64_t)a.hkv * a.num_blocks * kHeadDim;  // lo part follows the hi part
   float* out_row = a.scores + ((int64_t)h * a.num_qblocks + gq) * a.max_blocks;
   const int ncols = I + 1;
-  const int ntiles = (ncols + kJT - 1) / kJT;
+  const int ntiles_row = (ncols + kJT - 1) / kJT;
+  const int tile0 = (int)(((int64_t)part * ntiles_row) / a.cparts);
+  const int tile1 = (int)(((int64_t)(part + 1) * ntiles_row) / a.cparts);
+  if (tile0 >= tile1) return;  // whole workgroup: no barrier is skipped by part of it
   const int nchunks = 4 * a.group;  // 32-row chunks: (head, 32-token slice)
 
   // Tile t of both terms = 64 segments of 1 KiB (4 key rows each); wave w
@@ -250,13 +258,13 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       csc[rc] = sc;
     }
 
-    stage(0, 0);
+    stage(tile0, tile0 & 1);
     wait_vm();
     __syncthreads();
 
-    for (int tile = 0; tile < ntiles; ++tile) {
+    for (int tile = tile0; tile < tile1; ++tile) {
       const int buf = tile & 1;
-      if (tile + 1 < ntiles) stage(tile + 1, buf ^ 1);
+      if (tile + 1 < tile1) stage(tile + 1, buf ^ 1);
       const int njc = min(kJC, (ncols - tile * kJT + 31) >> 5);
       const u16* bh = sm.kb[buf][0];
       const u16* bl = sm.kb[buf][1];
@@ -314,8 +322,14 @@ hipError_t launch_scores_t(const ScoresArgs& a, dim3 grid, hipStream_t st) {
 
 hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
                          const u16* k_mean_bf16, float* scores, hipStream_t st) {
-  const dim3 grid((unsigned)(g.hkv * g.num_qblocks));
+  // A launch with at most 128 (kv head, query block) rows (small chunks)
+  // splits each row's key tiles over floor(256 / rows) workgroups (at most
+  // 16), so that every CU has work; whole prompts never split.
+  const int64_t rows = (int64_t)g.hkv * g.num_qblocks;
+  const int cparts = 2 * rows > 256 ? 1 : (int)std::min<int64_t>(16, 256 / rows);
+  const dim3 grid((unsigned)(rows * cparts));
   ScoresArgs a;
+  a.cparts = cparts;
   a.m = m;
   a.q = q;
   a.q_scale = q_scale;
