@@ -140,10 +140,22 @@ def gpu_setup(spec, threads=None, ctx=None, attn_splits=0):
     return w, pipe, t_gen
 
 
-def time_steps(pipe, alpha, correction, steps, warmup, sinks=256, local=512):
+def time_steps(pipe, alpha, correction, steps, warmup, sinks=256, local=512, select=None):
+    """select: None for the max-based threshold (alpha), else ("topk", k) or
+    ("topp", p) for the ranked selections."""
     import torch
+
+    def do_select():
+        if select is None:
+            pipe.select(alpha, sinks, local)
+        elif select[0] == "topk":
+            pipe.select_topk(int(select[1]), sinks, local)
+        else:
+            pipe.select_topp(float(select[1]), sinks, local)
     for _ in range(warmup):
-        pipe.run(alpha, sinks, local, correction)
+        pipe.discover()
+        do_select()
+        pipe.attend(correction, True)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -154,7 +166,7 @@ def time_steps(pipe, alpha, correction, steps, warmup, sinks=256, local=512):
         e[0].record(st)
         pipe.discover()
         e[1].record(st)
-        pipe.select(alpha, sinks, local)
+        do_select()
         e[2].record(st)
         pipe.attend(correction, True)
         e[3].record(st)
@@ -223,6 +235,9 @@ def main():
                     help="also time the alpha sweep x correction (written to --sweep-out)")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select", default="threshold", metavar="MODE",
+                    help="block selection: threshold (alpha), topk:K or topp:P (the ranked "
+                         "strategies the max-based threshold is compared with)")
     ap.add_argument("--attn-splits", type=int, default=0,
                     help="KV split of the attention: 0 automatic, 1 never, n parts per row")
     ap.add_argument("--chunk-ctx", type=int, default=None, metavar="TOKENS",
@@ -253,7 +268,12 @@ def main():
                                                for L in spec.seqlens]
     w, pipe, t_gen = gpu_setup(spec, ctx=ctx, attn_splits=args.attn_splits)
     print(f"# generated {spec.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
-    t = time_steps(pipe, args.alpha, correction, args.steps, args.warmup)
+    select = None
+    if args.select != "threshold":
+        mode, val = args.select.split(":")
+        assert mode in ("topk", "topp"), args.select
+        select = (mode, float(val))
+    t = time_steps(pipe, args.alpha, correction, args.steps, args.warmup, select=select)
     rp, ci = pipe.csr()
     kp, cp = kept_pairs(rp, ci, spec, ctx)
     d = spec.head_dim
@@ -317,6 +337,9 @@ def main():
     }
     if args.attn_splits:
         line["config"]["attn_splits"] = args.attn_splits
+    if select is not None:
+        line["config"]["select"] = args.select
+        line["roofline"]["traffic"] = None
     if ctx is not None:
         line["config"]["chunk"] = {"cached_tokens": ctx, "query_tokens":
                                    [L - c for L, c in zip(spec.seqlens, ctx)]}
@@ -335,7 +358,7 @@ def main():
                                eff_tflops=4 * d * k2 / (ts["step_ms"] * 1e-3) / 1e12, **ts)
                     f.write(json.dumps(rec) + "\n")
                     print("# sweep " + json.dumps(rec), file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline and ctx is None:
+    if not args.no_cpu_baseline and ctx is None and select is None:
         line["cpu_baseline"] = cpu_baseline(w, args.alpha, correction, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)
 

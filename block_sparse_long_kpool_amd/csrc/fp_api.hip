@@ -281,6 +281,50 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean, const flo
                     "select");
 }
 
+namespace {
+int select_ranked(const fp_problem* p, const float* block_scores, int mode, int32_t top_k, float top_p,
+                  int32_t sink_tokens, int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx,
+                  int64_t col_capacity, void* ws, size_t ws_bytes, void* stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st) return st;
+  if (!block_scores || !row_ptr || !col_idx) return fail(FP_ERR_INVALID, "fp_select_top%c: a tensor pointer is NULL", mode ? 'p' : 'k');
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(FP_ERR_INVALID, "sink_tokens and local_tokens must be >= 0");
+  if (mode == 0 && top_k < 0) return fail(FP_ERR_INVALID, "top_k must be >= 0 (got %d)", top_k);
+  if (mode == 1 && !(top_p == top_p)) return fail(FP_ERR_INVALID, "top_p is NaN");
+  const int64_t cap = fp_csr_capacity(p);
+  if (col_capacity < cap)
+    return fail(FP_ERR_CAPACITY, "col_capacity %lld < %lld (every causal block kept)",
+                (long long)col_capacity, (long long)cap);
+  if ((st = check_ws(g, FP_WS_SELECT, ws, ws_bytes))) return st;
+  SelectWs w;
+  ws_layout(g, FP_WS_SELECT, ws, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int n_sink = (sink_tokens + kBlock - 1) / kBlock;
+  const int n_local = std::max(1, (local_tokens + kBlock - 1) / kBlock);
+  const SeqMap m = seq_map(p, w.kboff, w.qboff);
+  if ((st = hip_status(launch_plan(m, s), "plan"))) return st;
+  return hip_status(launch_select_ranked(g, m, block_scores, mode, top_k, top_p, n_sink, n_local, w.bits,
+                                         w.counts, row_ptr, col_idx, s),
+                    "ranked select");
+}
+}  // namespace
+
+int fp_select_topk(const fp_problem* p, const float* block_scores, int32_t top_k, int32_t sink_tokens,
+                   int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return select_ranked(p, block_scores, 0, top_k, 0.f, sink_tokens, local_tokens, row_ptr, col_idx,
+                       col_capacity, ws, ws_bytes, stream);
+}
+
+int fp_select_topp(const fp_problem* p, const float* block_scores, float top_p, int32_t sink_tokens,
+                   int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return select_ranked(p, block_scores, 1, 0, top_p, sink_tokens, local_tokens, row_ptr, col_idx,
+                       col_capacity, ws, ws_bytes, stream);
+}
+
 int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* row_ptr, const int32_t* col_idx, const float* k_mean,
                          const float* v_mean, int32_t mean_correction, void* out, float* lse, void* ws,

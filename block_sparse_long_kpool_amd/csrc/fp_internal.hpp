@@ -236,6 +236,12 @@ hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, cons
                          int n_local, uint32_t* keep_bits, int32_t* counts, int32_t* row_ptr,
                          int32_t* col_idx, hipStream_t st);
 
+// Top-k (mode 0) / top-p (mode 1) selection from the scores, then the same
+// scan and compaction as the threshold path.
+hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float* scores, int mode,
+                                int top_k, float top_p, int n_sink, int n_local, uint32_t* keep_bits,
+                                int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);
+
 // Block offsets of the map plus bf16 copies of the pooled keys / values.
 hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_mean,
                             const float* v_mean, u16* km16, u16* vm16, hipStream_t st);

@@ -303,6 +303,131 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   }
 }
 
+// Ranked selection: top-k / top-p, the prior methods' strategies that the
+// FlashPrefill summary (section 二) contrasts with the max-based threshold
+// and its ablation 4.4 compares against.  One workgroup per CSR row sorts the
+// row's scores (bitonic sort in LDS, descending, ties toward the lower J: the
+// key is the order-preserving image of the float above the complement of J)
+// and keeps the forced blocks plus
+//   top-k: the first k non-forced blocks of the ranking, or
+//   top-p: the shortest ranked prefix (all causal blocks) whose share of
+//          sum_J e^{L_IJ} reaches p (partial sums in a fixed order).
+// The decisions use the scores as given (the fast fp32 path): entries within
+// its error of the cut may rank differently from exact arithmetic.
+constexpr int kRankThreads = 256;
+struct RankSmem {
+  unsigned long long key[kMaxBlocksPerSeq];
+  uint32_t keep[kMaxBlocksPerSeq / 32];
+  float part[kRankThreads];
+  float off[kRankThreads];
+  int cut;
+};
+
+template <int MODE>  // 0: top-k, 1: top-p
+__global__ __launch_bounds__(kRankThreads) void rank_kernel(
+    SeqMap m, int64_t num_qblocks, int max_blocks, const float* __restrict__ scores, int top_k,
+    float top_p, int n_sink, int n_local, uint32_t* __restrict__ keep_bits,
+    int32_t* __restrict__ counts) {
+  extern __shared__ __attribute__((aligned(16))) char rank_smem[];
+  RankSmem& sm = *reinterpret_cast<RankSmem*>(rank_smem);
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const QBlock qb = query_block(m, (int)(row % num_qblocks));
+  const int I = qb.I;
+  const int ncols = I + 1;
+  int P = 1;
+  while (P < ncols) P <<= 1;
+  const float* L = scores + row * max_blocks;
+  auto forced = [&](int J) { return J < n_sink || I - J < n_local; };
+  const int words = (max_blocks + 31) >> 5;
+  for (int i = tid; i < P; i += kRankThreads) {
+    unsigned long long k = 0;  // padding and excluded entries sort last
+    if (i < ncols && (MODE == 1 || !forced(i))) {
+      uint32_t b = __float_as_uint(L[i]);
+      b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+      k = ((unsigned long long)b << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+    }
+    sm.key[i] = k;
+  }
+  for (int w = tid; w < words; w += kRankThreads) sm.keep[w] = 0u;
+  __syncthreads();
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kRankThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = sm.key[i], b = sm.key[ixj];
+          if (((i & kk) == 0) ? (a < b) : (a > b)) {
+            sm.key[i] = b;
+            sm.key[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  auto block_of = [&](int i) { return (int)(0xFFFFFFFFu - (uint32_t)(sm.key[i] & 0xFFFFFFFFull)); };
+  int nkeep = 0;  // ranked entries kept: sorted positions 0 .. nkeep-1
+  if constexpr (MODE == 0) {
+    // forced blocks: the sinks J < n_sink and the window J > I - n_local
+    const int nf = min(n_sink, ncols) + max(0, ncols - max(n_sink, I - n_local + 1));
+    nkeep = min(max(top_k, 0), ncols - nf);
+  } else {
+    if (top_p > 0.f) {
+      // thread t sums the sorted positions [t * seg, (t + 1) * seg)
+      const int seg = (ncols + kRankThreads - 1) / kRankThreads;
+      const float lmax = L[block_of(0)];
+      const int i0 = tid * seg, i1 = min(ncols, i0 + seg);
+      float acc = 0.f;
+      for (int i = i0; i < i1; ++i) acc += __expf(L[block_of(i)] - lmax);
+      sm.part[tid] = acc;
+      if (tid == 0) sm.cut = ncols - 1;
+      __syncthreads();
+      if (tid == 0) {
+        float run = 0.f;
+        for (int t = 0; t < kRankThreads; ++t) {
+          sm.off[t] = run;
+          run += sm.part[t];
+        }
+        sm.part[0] = run;  // total (part[0] already consumed into off[1])
+      }
+      __syncthreads();
+      const float target = top_p * sm.part[0];
+      float cum = sm.off[tid];
+      for (int i = i0; i < i1; ++i) {
+        cum += __expf(L[block_of(i)] - lmax);
+        if (cum >= target) {
+          atomicMin(&sm.cut, i);
+          break;
+        }
+      }
+      __syncthreads();
+      nkeep = sm.cut + 1;
+    }
+  }
+  for (int i = tid; i < nkeep; i += kRankThreads) {
+    const int J = block_of(i);
+    atomicOr(&sm.keep[J >> 5], 1u << (J & 31));
+  }
+  for (int J = tid; J < ncols; J += kRankThreads)
+    if (forced(J)) atomicOr(&sm.keep[J >> 5], 1u << (J & 31));
+  __syncthreads();
+  uint32_t* bits = keep_bits + row * words;
+  int cnt = 0;
+  for (int w = tid; w < words; w += kRankThreads) {
+    const uint32_t v = sm.keep[w];
+    bits[w] = v;
+    cnt += __popc(v);
+  }
+  sm.part[tid] = (float)cnt;  // exact: counts are small integers
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int t = 0; t < kRankThreads; ++t) tot += (int)sm.part[t];
+    counts[row] = tot;
+  }
+}
+
 // Exclusive scan of counts[nrows] -> row_ptr[nrows + 1] (one workgroup).
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
                                                     int64_t nrows, int32_t* __restrict__ row_ptr) {
@@ -364,6 +489,34 @@ __global__ __launch_bounds__(256) void compact_kernel(int64_t nrows, int max_blo
 }
 
 }  // namespace
+
+hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float* scores, int mode,
+                                int top_k, float top_p, int n_sink, int n_local, uint32_t* keep_bits,
+                                int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
+  const unsigned nwg = (unsigned)g.num_rows;
+  const size_t shm = sizeof(RankSmem);
+  static bool attr_set[2] = {false, false};
+  const void* fn = mode == 0 ? (const void*)rank_kernel<0> : (const void*)rank_kernel<1>;
+  if (!attr_set[mode]) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set[mode] = true;
+  }
+  if (mode == 0)
+    hipLaunchKernelGGL(rank_kernel<0>, dim3(nwg), dim3(kRankThreads), shm, st, m, g.num_qblocks,
+                       g.max_blocks, scores, top_k, top_p, n_sink, n_local, keep_bits, counts);
+  else
+    hipLaunchKernelGGL(rank_kernel<1>, dim3(nwg), dim3(kRankThreads), shm, st, m, g.num_qblocks,
+                       g.max_blocks, scores, top_k, top_p, n_sink, n_local, keep_bits, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, g.num_rows, row_ptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3(nwg), dim3(256), 0, st, g.num_rows, g.max_blocks,
+                     keep_bits, row_ptr, col_idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
                          const float* k_mean, const float* scores, float alpha, int n_sink,

@@ -12,7 +12,7 @@ from dataclasses import dataclass
 from typing import Optional
 
 from ._binding import (FP_WS_ATTN, FP_WS_DISCOVER, FP_WS_SELECT, Problem, fp_discover,
-                       fp_select, fp_sparse_attn_paged)
+                       fp_select, fp_select_topk, fp_select_topp, fp_sparse_attn_paged)
 
 
 @dataclass
@@ -98,6 +98,14 @@ class Pipeline:
     def select(self, alpha: float, sink_tokens: int = 256, local_tokens: int = 512, stream=None):
         fp_select(self.problem, self.db.q, self.k_mean, self.scores, alpha, sink_tokens,
                   local_tokens, self.row_ptr, self.col_idx, self.ws[FP_WS_SELECT], stream)
+
+    def select_topk(self, top_k: int, sink_tokens: int = 256, local_tokens: int = 512, stream=None):
+        fp_select_topk(self.problem, self.scores, top_k, sink_tokens, local_tokens, self.row_ptr,
+                       self.col_idx, self.ws[FP_WS_SELECT], stream)
+
+    def select_topp(self, top_p: float, sink_tokens: int = 256, local_tokens: int = 512, stream=None):
+        fp_select_topp(self.problem, self.scores, top_p, sink_tokens, local_tokens, self.row_ptr,
+                       self.col_idx, self.ws[FP_WS_SELECT], stream)
 
     def attend(self, correction: bool = True, with_lse: bool = True, stream=None):
         d = self.db

@@ -194,6 +194,34 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean,
               int64_t col_capacity, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp_select_topk / fp_select_topp -- ranked block selection, the strategies
+ * of the prior methods that the max-based threshold replaces (FlashPrefill
+ * summary "长上下文加速 28 倍", section 二: top-k needs a sort, top-p a
+ * running probability sum; its ablation 4.4 compares them with fp_select),
+ * for comparisons on the same scores.
+ *
+ * Row (h, s, I) ranks its causal blocks J <= I by block_scores (descending,
+ * ties toward the lower J) and keeps the forced blocks (sinks and local
+ * window, as in fp_select) plus
+ *   top-k: the first top_k ranked blocks that are not forced (all of them if
+ *          fewer), or
+ *   top-p: the shortest ranked prefix of all causal blocks whose share of
+ *          sum_J e^{L_IJ} reaches top_p (top_p <= 0: forced blocks only).
+ * Unlike fp_select, the decisions use the fp32 scores as given, without a
+ * float64 re-check: blocks whose scores lie within the fast path's error of
+ * the cut may rank differently from exact arithmetic.  Outputs, capacity and
+ * workspace (FP_WS_SELECT) as for fp_select; q and k_mean are not needed.
+ */
+int fp_select_topk(const fp_problem* p, const float* block_scores, int32_t top_k,
+                   int32_t sink_tokens, int32_t local_tokens, int32_t* row_ptr,
+                   int32_t* col_idx, int64_t col_capacity, void* ws, size_t ws_bytes,
+                   void* stream);
+int fp_select_topp(const fp_problem* p, const float* block_scores, float top_p,
+                   int32_t sink_tokens, int32_t local_tokens, int32_t* row_ptr,
+                   int32_t* col_idx, int64_t col_capacity, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
  * fp_sparse_attn_paged -- sparse causal attention over the listed blocks with
  * block-mean correction.
  *

@@ -238,3 +238,65 @@ def test_small_chunk_auto_split():
                                              num_kv_heads=2, page_size=64, seed=150)), (8192,))
     g = run_gpu(w, 0.1)
     compare(w, g, 0.1)
+
+
+RANKED = [("topk", 0), ("topk", 3), ("topk", 100000), ("topp", 0.0), ("topp", 0.5), ("topp", 0.95)]
+
+
+@pytest.mark.parametrize("mode,param", RANKED, ids=[f"{m}_{p}" for m, p in RANKED])
+def test_ranked_selection_parity(mode, param):
+    """Top-k / top-p selection on the GPU's scores: the lists equal the
+    oracle's ranking of the same fp32 scores (top-p: up to the fp32 rounding
+    of the running sum at the cut), and attention over them matches the
+    oracle."""
+    import torch
+    from block_sparse_long_kpool_amd import Pipeline, upload
+    from oracle import OracleProblem, forced_blocks, rank_order, run_pipeline, select_row_topk
+    log(f"case ranked {mode} {param}")
+    w = make_workload(custom_spec(name="ranked", seqlens=(1500, 640, 129), num_q_heads=8,
+                                  num_kv_heads=2, page_size=16, paging="permute", seed=160))
+    pipe = Pipeline(upload(w, "cuda"))
+    pipe.discover()
+    if mode == "topk":
+        pipe.select_topk(param)
+    else:
+        pipe.select_topp(param)
+    pipe.attend()
+    torch.cuda.synchronize()
+    rp, ci = pipe.csr()
+    scores = pipe.scores.cpu().numpy().astype(np.float64)
+    out = pipe.out.float().cpu().numpy()
+    lse = pipe.lse.cpu().numpy()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    prob = OracleProblem.from_workload(w)
+    qoff = prob.query_block_offsets()
+    for h in range(prob.hkv):
+        for s_ in range(prob.num_seqs):
+            for I in prob.query_blocks(s_):
+                row = prob.row_index(h, s_, I)
+                got = set(ci[rp[row]:rp[row + 1]].tolist())
+                L = scores[h, int(qoff[s_]) + I, :I + 1]
+                forced = set(np.nonzero(forced_blocks(I, 256, 512, 128))[0].tolist())
+                if mode == "topk":
+                    want = set(select_row_topk(L, I, param, 256, 512, 128).tolist())
+                    assert got == want, (h, s_, I)
+                else:
+                    order = rank_order(L, I)
+                    if param <= 0:
+                        assert got == forced, (h, s_, I)
+                        continue
+                    cum = np.cumsum(np.exp(L[order] - L.max()))
+                    lo = int(np.searchsorted(cum, param * cum[-1] * (1 - 1e-4)))
+                    hi = int(np.searchsorted(cum, param * cum[-1] * (1 + 1e-4)))
+                    ok = [set(order[:m + 1].tolist()) | forced for m in range(lo, min(hi, I) + 1)]
+                    assert got in ok, (h, s_, I)
+    res = run_pipeline(prob, 0.1, given_csr=(rp, ci))
+    G = w.spec.group
+    worst = wl = 0.0
+    for (h, s_, I), r in res.items():
+        toks = int(w.cu_seqlens[s_]) + I * 128 + np.arange(r["out"].shape[1])
+        og = out[toks][:, h * G:(h + 1) * G].transpose(1, 0, 2)
+        worst = max(worst, float(np.abs(og - r["out"]).max()))
+        wl = max(wl, float(np.abs(lse[h * G:(h + 1) * G][:, toks] - r["lse"]).max()))
+    log(f"  out err {worst:.3g} lse err {wl:.3g}")
+    assert worst <= 2e-2 and wl <= 5e-2
