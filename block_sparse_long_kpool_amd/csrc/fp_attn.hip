@@ -30,6 +30,11 @@
 //     ds_read_b64_tr_b16 (16x4 transposes inside 16-lane groups).
 //   * correction tiles: 128 pooled keys/values (bf16) per tile with a
 //     log2(n_J) bias; listed blocks and J > I are masked to -inf.
+//   * rows: query blocks of the call (a chunk's blocks after a cached prefix,
+//     or whole prompts); keys are every cached position up to the row.
+//   * KV split (small launches): a row's tile list is cut into contiguous
+//     parts, one workgroup each; parts write fp32 partial outputs and lse,
+//     merged by attn_combine_kernel.
 #include <algorithm>
 #include <type_traits>
 

@@ -9,7 +9,9 @@
 // with x_rJ = softmax_scale * q_r . kbar_J.
 //
 // gfx950 design:
-//   * one workgroup (8 waves) owns one (h, I) and ALL its rows; the rows go
+//   * one workgroup (8 waves) owns one (h, I) and ALL its rows (small
+//     launches split the key tiles of a row over several workgroups, since
+//     columns are independent); the rows go
 //     in passes of 8 waves x 2 chunks x 32 rows, each wave holding the Q
 //     fragments of its two chunks in registers for the whole pass, so Q is
 //     read from HBM once (passes = g / 4).
