@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int h = (int)(row_ord % a.hkv);
   const int gq = (int)(a.num_qblocks - 1 - row_ord / a.hkv);
   const int64_t row = (int64_t)h * a.num_qblocks + gq;
-  const QBlock qb = query_block(a.m, gq);
+  const QBlock qb = uniform_block(query_block(a.m, gq));
   const int s = qb.s;
   const int I = qb.I;
   const int len = qb.klen;  // keys: cached prefix + this chunk
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
 
   const int hh = 2 * pack + (wave * RC) / 4;
   const bool head_ok = hh < a.group;
-  const int hq_idx = h * a.group + (head_ok ? hh : 0);
+  const int hq_idx = __builtin_amdgcn_readfirstlane(h * a.group + (head_ok ? hh : 0));  // wave-uniform
   const int tbase = 32 * ((wave * RC) % 4);
 
   // ---- Q^T fragments (B operand), kept for the whole kernel ----
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int rc = 0; rc < RC; ++rc) {
     const int t0 = tbase + 32 * rc;
-    nvalid[rc] = head_ok ? max(0, min(32, nI - t0)) : 0;
+    nvalid[rc] = __builtin_amdgcn_readfirstlane(head_ok ? max(0, min(32, nI - t0)) : 0);  // wave-uniform
     const bool rvalid = col < nvalid[rc];
     const int64_t e0 = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim + 64 * half;
     if constexpr (kFp8) {
@@ -252,7 +252,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  const int npooled = a.correction ? sm.npooled : 0;
+  // wave-uniform counts: keep them in scalar registers
+  const int npooled = a.correction ? __builtin_amdgcn_readfirstlane(sm.npooled) : 0;
   const int ntiles = nkept + npooled;
   // KV split: this workgroup takes tiles [tbeg, tend) of the row's list
   // (contiguous parts balanced by tile count; all of it without a split)
@@ -654,6 +655,11 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   }
   for (int t = max(nkept, tbeg); t < tend; ++t) iterate(t, std::true_type{}, std::false_type{});
 
+  // The lane's row index again, opaque to the compiler: otherwise it keeps
+  // the 64-bit row addresses of the Q loads live through the whole loop
+  // (two register pairs, which spill in the e4m3 instances).
+  int ecol = col;
+  asm volatile("" : "+v"(ecol));
   if (a.splits > 1) {
     // part of a split row: O_part = acc / l and lse_part in fp32 for the
     // combine pass (an empty part: O_part = 0, lse_part = -inf)
@@ -661,8 +667,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     for (int rc = 0; rc < RC; ++rc) {
       const float l_tot = l_run[rc] + __shfl_xor(l_run[rc], 32, 64);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      if (col >= nvalid[rc]) continue;
-      const int64_t tok = tok0 + tbase + 32 * rc + col;
+      if (ecol >= nvalid[rc]) continue;
+      const int64_t tok = tok0 + tbase + 32 * rc + ecol;
       float* ob = a.opart + (((int64_t)split * a.total_tokens + tok) * a.hq + hq_idx) * kHeadDim;
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc)
@@ -686,8 +692,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     for (int rc = 0; rc < RC; ++rc) {
       const float l_tot = l_run[rc] + __shfl_xor(l_run[rc], 32, 64);
       const float inv = 1.f / l_tot;
-      if (col >= nvalid[rc]) continue;
-      const int64_t tok = tok0 + tbase + 32 * rc + col;
+      if (ecol >= nvalid[rc]) continue;
+      const int64_t tok = tok0 + tbase + 32 * rc + ecol;
       const int64_t obase = (tok * a.hq + hq_idx) * (int64_t)kHeadDim;
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {

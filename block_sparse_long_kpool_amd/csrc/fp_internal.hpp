@@ -107,6 +107,22 @@ __device__ __forceinline__ QBlock query_block(const SeqMap& m, int gq) {
   return r;
 }
 
+// The same block with every field in scalar registers (the values are
+// wave-uniform; loaded through vector memory they would otherwise occupy
+// VGPRs for the whole kernel).
+__device__ __forceinline__ QBlock uniform_block(const QBlock& q) {
+  QBlock r;
+  r.s = __builtin_amdgcn_readfirstlane(q.s);
+  r.I = __builtin_amdgcn_readfirstlane(q.I);
+  r.nI = __builtin_amdgcn_readfirstlane(q.nI);
+  r.klen = __builtin_amdgcn_readfirstlane(q.klen);
+  r.kb0 = __builtin_amdgcn_readfirstlane(q.kb0);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)q.tok0);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)q.tok0 >> 32));
+  r.tok0 = (int64_t)(((uint64_t)hi << 32) | lo);
+  return r;
+}
+
 // Both block prefixes of SeqMap, by one workgroup of 256 threads.
 __device__ __forceinline__ void plan_offsets(const SeqMap& m) {
   __shared__ int bufk[256], bufq[256];
