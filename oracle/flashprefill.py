@@ -58,6 +58,13 @@ design notes):
      the lower J; top-k adds the k best non-forced blocks to the forced ones;
      top-p adds the fewest best causal blocks whose share of sum_J e^{L_IJ}
      reaches p.  Both keep the same sink / local safety net.
+  R22 per-query-head lists (the alternative to R4 that the index-memory
+     figure of [V2a]'s CSR / paged-KV section suggests: its CSR size at 128K
+     fits one list per query head, while PackGQA implies one per KV group):
+     rows(I) are the tokens of block I for that query head alone; the head's
+     keys, values and pooled blocks are those of its KV head hq // g; each
+     head attends over its own list and corrects with its own pruned blocks.
+     Library rows are then (query head, sequence, query block).
   R20 chunked prefill ([V2a] chunked-prefill passage): a chunk's queries are
      positions ctx .. ctx + qlen - 1 of a sequence whose first ctx tokens
      (a multiple of B) are already cached.  Pooling covers every cached key
@@ -157,6 +164,8 @@ class OracleProblem:
     # selected and attended (reading R20: ctx is a multiple of B, so every
     # query block is a whole block of the sequence).  None: whole prompts.
     ctx_lens: Optional[np.ndarray] = None
+    # Reading R22: one index list per query head instead of per KV group.
+    head_lists: bool = False
 
     @classmethod
     def from_workload(cls, w) -> "OracleProblem":
@@ -217,7 +226,8 @@ class OracleProblem:
         return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
 
     def row_index(self, h: int, s: int, I: int) -> int:
-        """Library row of (KV head, sequence, query block)."""
+        """Library row of (list owner, sequence, query block); the owner is the
+        KV head, or the query head under reading R22."""
         qoff = self.query_block_offsets()
         return h * int(qoff[-1]) + int(qoff[s]) + I - self.ctx(s) // self.block_size
 
@@ -256,6 +266,19 @@ class OracleProblem:
     def group_heads(self, h: int) -> List[int]:
         g = self.group
         return list(range(h * g, (h + 1) * g))
+
+    # List owners: KV heads (R4), or query heads under reading R22.
+    @property
+    def list_owners(self) -> int:
+        return self.hq if self.head_lists else self.hkv
+
+    def list_kv_head(self, o: int) -> int:
+        """KV head whose keys, values and pooled blocks list owner o uses."""
+        return o // self.group if self.head_lists else o
+
+    def list_heads(self, o: int) -> List[int]:
+        """Query heads whose rows list owner o scores and attends."""
+        return [o] if self.head_lists else self.group_heads(o)
 
 
 # ---------------------------------------------------------------------------
@@ -412,9 +435,11 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
                  given_csr: Optional[tuple] = None, cache: Optional[dict] = None) -> dict:
     """Run pool -> score -> select -> attend.
 
-    rows: optional list of (h, s, I) to evaluate (default: all).  For each
+    rows: optional list of (h, s, I) to evaluate (default: all); h is the
+    list owner (the KV head, or the query head under R22).  For each
     evaluated row the result holds the L scores, the kept list, the band
-    flags, and (if `attend`) out [G, nI, d] / lse [G, nI] for the KV group.
+    flags, and (if `attend`) out [G, nI, d] / lse [G, nI] for the owner's
+    query heads (G = g, or 1 under R22).
     given_csr: optional (row_ptr, col_idx) in the library's row order
     (h, global block); when set, attention uses those lists instead of the
     oracle's own selection (to compare attention alone).
@@ -423,7 +448,7 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
     """
     B = prob.block_size
     if rows is None:
-        rows = [(h, s, I) for h in range(prob.hkv) for s in range(prob.num_seqs)
+        rows = [(h, s, I) for h in range(prob.list_owners) for s in range(prob.num_seqs)
                 for I in prob.query_blocks(s)]
     if cache is None:
         cache = {}
@@ -441,10 +466,10 @@ def run_pipeline(prob: OracleProblem, alpha: float, sink_tokens: int = 256,
 
     results = {}
     for (h, s, I) in sorted(rows, key=lambda r: (r[1], r[0], r[2])):
-        K, V, km, vm, cnt = seq_data(s, h)
+        K, V, km, vm, cnt = seq_data(s, prob.list_kv_head(h))
         nI = int(cnt[I])
         pos = I * B + np.arange(nI)
-        qg = prob.queries(s, prob.group_heads(h), pos)            # [G, nI, d]
+        qg = prob.queries(s, prob.list_heads(h), pos)             # [G, nI, d]
         sc = block_scores(qg.reshape(-1, prob.d), km[:I + 1], prob.scale)
         kept, band = select_row(sc["L"], I, alpha, sink_tokens, local_tokens, B)
         res = {"L": sc["L"], "M": sc["M"], "S": sc["S"], "Shat": sc["Shat"],
@@ -481,15 +506,15 @@ def pooled_all(prob: OracleProblem):
 
 
 def csr_from_results(prob: OracleProblem, results: dict):
-    """Library-order CSR (rows (h, s, I)) from a full run_pipeline result."""
+    """Library-order CSR (rows (owner, s, I)) from a full run_pipeline result."""
     nq = int(prob.query_block_offsets()[-1])
-    counts = np.zeros(prob.hkv * nq, dtype=np.int64)
+    counts = np.zeros(prob.list_owners * nq, dtype=np.int64)
     lists = {}
     for (h, s, I), r in results.items():
         row = prob.row_index(h, s, I)
         lists[row] = r["kept"]
         counts[row] = len(r["kept"])
-    row_ptr = np.zeros(prob.hkv * nq + 1, dtype=np.int64)
+    row_ptr = np.zeros(prob.list_owners * nq + 1, dtype=np.int64)
     row_ptr[1:] = np.cumsum(counts)
     col = np.zeros(int(row_ptr[-1]), dtype=np.int64)
     for row, kept in lists.items():
