@@ -54,6 +54,7 @@ class FpProblemC(ctypes.Structure):
         ("ctx_lens_host", ctypes.POINTER(ctypes.c_int32)),
         ("ctx_lens_dev", ctypes.c_void_p),
         ("attn_splits", ctypes.c_int32),
+        ("head_lists", ctypes.c_int32),
     ]
 
 
@@ -128,7 +129,7 @@ class Problem:
                  page_table, page_size: int, num_pages: int, qk_dtype: str, v_dtype: str,
                  out_dtype: str, cu_seqlens_dev=None, q_scale=None, k_scale=None,
                  softmax_scale: float = 0.0, device=None, ctx_lens: Optional[Sequence[int]] = None,
-                 attn_splits: int = 0):
+                 attn_splits: int = 0, head_lists: bool = False):
         import torch
         self.device = device or page_table.device
         cu = [int(x) for x in cu_seqlens]
@@ -147,6 +148,9 @@ class Problem:
         self.k_scale = k_scale
         self.qk_dtype, self.v_dtype, self.out_dtype = qk_dtype, v_dtype, out_dtype
         self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        # index-list owners: KV heads, or query heads with head_lists
+        self.head_lists = bool(head_lists)
+        self.list_owners = num_q_heads if head_lists else num_kv_heads
         self.total_tokens = cu[-1]
         c = FpProblemC()
         c.num_seqs = len(cu) - 1
@@ -170,6 +174,7 @@ class Problem:
             c.ctx_lens_host = self.ctx_host
             c.ctx_lens_dev = _ptr(self.ctx_dev)
         c.attn_splits = attn_splits
+        c.head_lists = 1 if head_lists else 0
         self.c = c
         self.lib = load_library()
 

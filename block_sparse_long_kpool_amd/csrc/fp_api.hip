@@ -87,7 +87,12 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   g->num_blocks = nblk;
   g->num_qblocks = nqblk;
   g->max_blocks = maxn;
-  g->num_rows = nqblk * p->num_kv_heads;
+  if (p->head_lists != 0 && p->head_lists != 1)
+    return fail(FP_ERR_INVALID, "head_lists must be 0 or 1 (got %d)", p->head_lists);
+  g->lists = p->head_lists ? p->num_q_heads : p->num_kv_heads;
+  g->lgroup = p->head_lists ? 1 : p->num_q_heads / p->num_kv_heads;
+  g->kvdiv = p->head_lists ? p->num_q_heads / p->num_kv_heads : 1;
+  g->num_rows = nqblk * g->lists;
   g->total_tokens = cu[p->num_seqs];
   g->qk_dtype = qk;
   g->v_dtype = vd;
@@ -210,7 +215,7 @@ int64_t fp_csr_capacity(const fp_problem* p) {
     const int64_t i0 = ctx / kBlock;  // first query block
     c += n * (n + 1) / 2 - i0 * (i0 + 1) / 2;
   }
-  return c * g.hkv;
+  return c * g.lists;
 }
 
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which) {

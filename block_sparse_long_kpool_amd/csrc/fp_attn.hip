@@ -85,10 +85,11 @@ struct AttnArgs {
   float* lpart;  // splits > 1: [splits, Hq, T] partial lse (natural log; -inf for an empty part)
   int splits;    // workgroups per (row, head pack), each over a contiguous part of the tile list
   int64_t num_blocks;   // NK (pooled rows per KV head)
-  int64_t num_qblocks;  // NQ (CSR rows per KV head)
+  int64_t num_qblocks;  // NQ (CSR rows per list owner)
   int64_t total_tokens;
   int max_pages, page_size;
-  int hq, hkv, group, packs;
+  int hq, hkv, group, packs;  // group: query heads per index list (1 per query head)
+  int lists, kvdiv;           // list owners; owner o reads KV head o / kvdiv
   int correction;
   float softmax_scale;
 };
@@ -146,18 +147,19 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int pack = kq % a.packs;
   const int split = (kq / a.packs) % a.splits;
   const int64_t row_ord = (int64_t)(kq / a.packs / a.splits) * 8 + xcd;
-  const int64_t nrows = (int64_t)a.hkv * a.num_qblocks;
+  const int64_t nrows = (int64_t)a.lists * a.num_qblocks;
   if (row_ord >= nrows) return;
-  const int h = (int)(row_ord % a.hkv);
-  const int gq = (int)(a.num_qblocks - 1 - row_ord / a.hkv);
+  const int h = (int)(row_ord % a.lists);  // list owner (CSR row h * NQ + gq)
+  const int gq = (int)(a.num_qblocks - 1 - row_ord / a.lists);
   const int64_t row = (int64_t)h * a.num_qblocks + gq;
+  const int kvh = h / a.kvdiv;  // KV head of the owner's keys, values and pooled blocks
   const QBlock qb = uniform_block(query_block(a.m, gq));
   const int s = qb.s;
   const int I = qb.I;
   const int len = qb.klen;  // keys: cached prefix + this chunk
   const int nI = qb.nI;
   const int64_t tok0 = qb.tok0;
-  const int64_t pooled_base = (int64_t)h * a.num_blocks + qb.kb0;
+  const int64_t pooled_base = (int64_t)kvh * a.num_blocks + qb.kb0;
   const int kbeg = a.row_ptr[row];
   // a valid list holds at most I + 1 blocks (the LDS tile list is sized for it)
   const int nkept = min(max(a.row_ptr[row + 1] - kbeg, 0), I + 1);
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     const int p0 = J * kBlock + tid;
     const int p = p0 < len ? p0 : J * kBlock;
     const int cslot = page * psz + (small_pages ? (p & (psz - 1)) : (p % psz));
-    sm.slot[sbuf][tid] = ((int64_t)cslot * a.hkv + h) * kHeadDim;
+    sm.slot[sbuf][tid] = ((int64_t)cslot * a.hkv + kvh) * kHeadDim;
   };
   auto issue_tile = [&](int t, int buf) {
     const bool pooled = t >= nkept;
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   float c_pool = c_kept;
   if constexpr (kFp8) {
     const float qs = a.q_scale[hq_idx];
-    c_kept *= qs * a.k_scale[h];
+    c_kept *= qs * a.k_scale[kvh];
     c_pool *= qs;
   }
 
@@ -833,7 +835,7 @@ hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_m
 
 int attn_splits(const Geometry& g) {
   if (g.attn_splits > 0) return std::min(g.attn_splits, kAttnMaxSplits);
-  const int64_t wgs = ((g.hkv * g.num_qblocks + 7) / 8) * 8 * ((g.group + 1) / 2);
+  const int64_t wgs = ((g.lists * g.num_qblocks + 7) / 8) * 8 * ((g.lgroup + 1) / 2);
   if (2 * wgs > kAttnSplitTarget) return 1;
   return (int)std::min<int64_t>(kAttnMaxSplits, kAttnSplitTarget / wgs);
 }
@@ -868,11 +870,13 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   a.page_size = g.page_size;
   a.hq = g.hq;
   a.hkv = g.hkv;
-  a.group = g.group;
-  a.packs = (g.group + 1) / 2;
+  a.group = g.lgroup;
+  a.lists = g.lists;
+  a.kvdiv = g.kvdiv;
+  a.packs = (g.lgroup + 1) / 2;
   a.correction = correction;
   a.softmax_scale = g.softmax_scale;
-  const int64_t rows = (int64_t)g.hkv * g.num_qblocks;
+  const int64_t rows = (int64_t)g.lists * g.num_qblocks;
   const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs * a.splits);
   const size_t shm = sizeof(SharedMem);
 #define FP_ATTN(QD, VD, OD)                                                                    \

@@ -31,7 +31,11 @@ struct Geometry {
   int64_t num_blocks;    // NK = sum_s nk_s key blocks (pooled rows)
   int64_t num_qblocks;   // NQ = sum_s nq_s query blocks (score / CSR rows per KV head)
   int max_blocks;        // max_s nk_s
-  int64_t num_rows;      // Hkv * NQ
+  int64_t num_rows;      // lists * NQ (score / CSR rows)
+  // Index-list owners: the KV heads (lists = Hkv, lgroup = group query heads
+  // per list, kvdiv = 1) or, per query head, lists = Hq, lgroup = 1 and
+  // kvdiv = group (owner o reads KV head o / kvdiv).
+  int lists, lgroup, kvdiv;
   int64_t total_tokens;  // T (query tokens)
   int qk_dtype, v_dtype, out_dtype;
   float softmax_scale;

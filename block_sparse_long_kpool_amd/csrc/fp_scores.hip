@@ -60,7 +60,9 @@ struct ScoresArgs {
   float* scores;
   int64_t num_blocks;   // NK (pooled rows per KV head)
   int64_t num_qblocks;  // NQ (score rows per KV head)
-  int hq, hkv, group, max_blocks;
+  int hq, hkv, group, max_blocks;  // group: query heads per index list (1 per query head)
+  int lists, kvdiv;                // list owners (score rows per query block); owner o
+                                   // reads the pooled keys of KV head o / kvdiv
   int cparts;           // workgroups per (kv head, query block), each over a range of key tiles
   float logit_scale;
 };
@@ -203,14 +205,14 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   // heaviest rows (largest I of a sequence) first; the cparts workgroups of
   // a row take contiguous ranges of its key tiles (columns are independent)
   const int part = (int)(blockIdx.x % a.cparts);
-  const int64_t item = (int64_t)a.hkv * a.num_qblocks - 1 - blockIdx.x / a.cparts;
-  const int h = (int)(item % a.hkv);
-  const int gq = (int)(item / a.hkv);
+  const int64_t item = (int64_t)a.lists * a.num_qblocks - 1 - blockIdx.x / a.cparts;
+  const int h = (int)(item % a.lists);  // list owner
+  const int gq = (int)(item / a.lists);
   const QBlock qb = query_block(a.m, gq);
   const int I = qb.I;
   const int nI = qb.nI;
   const int64_t tok0 = qb.tok0;
-  const u16* kbase = a.kmean16 + ((int64_t)h * a.num_blocks + qb.kb0) * kHeadDim;
+  const u16* kbase = a.kmean16 + ((int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0) * kHeadDim;
   const int64_t lo_off = (int64_t)a.hkv * a.num_blocks * kHeadDim;  // lo part follows the hi part
   float* out_row = a.scores + ((int64_t)h * a.num_qblocks + gq) * a.max_blocks;
   const int ncols = I + 1;
@@ -327,7 +329,7 @@ hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, cons
   // A launch with at most 128 (kv head, query block) rows (small chunks)
   // splits each row's key tiles over floor(256 / rows) workgroups (at most
   // 16), so that every CU has work; whole prompts never split.
-  const int64_t rows = (int64_t)g.hkv * g.num_qblocks;
+  const int64_t rows = (int64_t)g.lists * g.num_qblocks;
   const int cparts = 2 * rows > 256 ? 1 : (int)std::min<int64_t>(16, 256 / rows);
   const dim3 grid((unsigned)(rows * cparts));
   ScoresArgs a;
@@ -341,7 +343,9 @@ hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, cons
   a.num_qblocks = g.num_qblocks;
   a.hq = g.hq;
   a.hkv = g.hkv;
-  a.group = g.group;
+  a.group = g.lgroup;
+  a.lists = g.lists;
+  a.kvdiv = g.kvdiv;
   a.max_blocks = g.max_blocks;
   a.logit_scale = g.softmax_scale;
   if (g.qk_dtype == FP_BF16) return launch_scores_t<FP_BF16>(a, grid, st);

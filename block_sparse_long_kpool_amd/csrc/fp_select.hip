@@ -174,7 +174,7 @@ __device__ double exact_score_wg(const void* q, const float* q_scale, const floa
 // of the row's bitmask and the count.
 template <int QDT>
 __global__ __launch_bounds__(kSelThreads) void decide_kernel(
-    SeqMap m, int hq, int hkv, int group, int64_t num_blocks, int64_t num_qblocks,
+    SeqMap m, int hq, int kvdiv, int group, int64_t num_blocks, int64_t num_qblocks,
     int max_blocks, float softmax_scale,
     const void* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ k_mean, const float* __restrict__ scores, float alpha, int n_sink,
@@ -252,7 +252,9 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   if (need) {
     const int nI = qb.nI;
     const int64_t tok0 = qb.tok0;
-    const float* kb = k_mean + ((int64_t)h * num_blocks + qb.kb0) * kHeadDim;
+    // list owner h: rows of its query heads h * group .. (group of them),
+    // pooled keys of its KV head h / kvdiv
+    const float* kb = k_mean + ((int64_t)(h / kvdiv) * num_blocks + qb.kb0) * kHeadDim;
     const double ref = (double)lmax;
     double emax = -INFINITY;
     for (int w = 0; w < nw_row; ++w) {
@@ -524,8 +526,8 @@ hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, cons
                          int32_t* col_idx, hipStream_t st) {
   const unsigned nwg = (unsigned)g.num_rows;
 #define FP_DEC(QD)                                                                              \
-  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, m, g.hq, g.hkv,  \
-                     g.group, g.num_blocks, g.num_qblocks, g.max_blocks, g.softmax_scale, q,   \
+  hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, m, g.hq, g.kvdiv, \
+                     g.lgroup, g.num_blocks, g.num_qblocks, g.max_blocks, g.softmax_scale, q,  \
                      q_scale, k_mean, scores, alpha, n_sink, n_local, keep_bits, counts)
   if (g.qk_dtype == FP_BF16) FP_DEC(FP_BF16);
   else if (g.qk_dtype == FP_E4M3) FP_DEC(FP_E4M3);

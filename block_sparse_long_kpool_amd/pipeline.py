@@ -66,7 +66,8 @@ def upload(batch, device="cuda", out_dtype: Optional[str] = None) -> DeviceBatch
 class Pipeline:
     """All device buffers of one batch shape, and the three calls in order."""
 
-    def __init__(self, db: DeviceBatch, softmax_scale: float = 0.0, attn_splits: int = 0):
+    def __init__(self, db: DeviceBatch, softmax_scale: float = 0.0, attn_splits: int = 0,
+                 head_lists: bool = False):
         import torch
         self.db = db
         dev = db.q.device
@@ -74,14 +75,16 @@ class Pipeline:
                                db.page_size, int(db.k_cache.shape[0]), db.qk_dtype, db.v_dtype,
                                db.out_dtype, cu_seqlens_dev=db.cu_seqlens, q_scale=db.q_scale,
                                k_scale=db.k_scale, softmax_scale=softmax_scale,
-                               ctx_lens=db.ctx_lens, attn_splits=attn_splits)
+                               ctx_lens=db.ctx_lens, attn_splits=attn_splits,
+                               head_lists=head_lists)
         p = self.problem
         N, NQ = p.num_blocks, p.num_query_blocks
         hkv, T, hq = db.num_kv_heads, p.total_tokens, db.num_q_heads
         f32 = torch.float32
         self.k_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
         self.v_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
-        self.scores = torch.empty((hkv, NQ, p.max_blocks), dtype=f32, device=dev)
+        # score rows per index-list owner (KV head, or query head with head_lists)
+        self.scores = torch.empty((p.list_owners, NQ, p.max_blocks), dtype=f32, device=dev)
         self.row_ptr = torch.empty(p.num_rows + 1, dtype=torch.int32, device=dev)
         self.col_idx = torch.empty(p.csr_capacity, dtype=torch.int32, device=dev)
         odt = torch.float32 if db.out_dtype == "f32" else torch.bfloat16

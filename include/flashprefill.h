@@ -51,12 +51,18 @@
  *       k_mean, v_mean [Hkv, N, 128] float32 (key block J of sequence s at
  *                  row kboff_s + J, kboff_s = sum of nk over earlier
  *                  sequences)
- *       block_scores   [Hkv, NQ, n_max] float32 (query block I of sequence s
+ *       block_scores   [Lo, NQ, n_max] float32 (query block I of sequence s
  *                  at row qboff_s + I - c_s/128, qboff_s = sum of nq over
  *                  earlier sequences; entry J for J <= I)
- *       row_ptr    [Hkv * NQ + 1] int32, rows ordered (kv head, sequence,
+ *       row_ptr    [Lo * NQ + 1] int32, rows ordered (list owner, sequence,
  *                  query block); col_idx int32 block indices inside the
  *                  sequence, ascending per row.
+ *     Lo, the list owners: Lo = Hkv (one index list per KV group, shared by
+ *     its Hq / Hkv query heads: the default) or Lo = Hq with head_lists = 1
+ *     (one list per query head, scored from that head's rows alone and used
+ *     by that head alone; owner hq reads KV head hq / (Hq / Hkv)).  This is
+ *     the reading of the V2 article's CSR index-memory figure, which fits
+ *     per-query-head lists; PackGQA tiles suggest per-group lists.
  *       out        [T, Hq, 128] dtype out_dtype
  *       lse        [Hq, T] float32 (natural log), optional
  *   - Query head hq reads KV head hq / (Hq / Hkv).
@@ -119,6 +125,10 @@ typedef struct {
   int32_t attn_splits;             /* KV split of fp_sparse_attn_paged: 0 = automatic,
                                       1 = never split, n = split every row into n
                                       parts (at most 8)                              */
+  int32_t head_lists;              /* 0: one index list per KV head (rows (kv head,
+                                      seq, block)); 1: one per query head (rows
+                                      (q head, seq, block)); every call of one
+                                      pass must use the same value               */
 } fp_problem;
 
 /* Supported dtype combinations (qk, v): (F32, F32), (BF16, BF16), (E4M3, BF16);
@@ -128,9 +138,9 @@ typedef struct {
 int64_t fp_num_blocks(const fp_problem* p);       /* N = sum_s nk_s (pooled rows) */
 int64_t fp_num_query_blocks(const fp_problem* p); /* NQ = sum_s nq_s              */
 int32_t fp_max_blocks(const fp_problem* p);       /* n_max                        */
-int64_t fp_num_rows(const fp_problem* p);         /* Hkv * NQ (CSR rows)          */
-int64_t fp_scores_elems(const fp_problem* p);     /* Hkv * NQ * n_max             */
-int64_t fp_csr_capacity(const fp_problem* p);     /* Hkv * sum over query blocks of
+int64_t fp_num_rows(const fp_problem* p);         /* Lo * NQ (CSR rows)           */
+int64_t fp_scores_elems(const fp_problem* p);     /* Lo * NQ * n_max              */
+int64_t fp_csr_capacity(const fp_problem* p);     /* Lo * sum over query blocks of
                                                      (I + 1): every causal block kept */
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which);
 const char* fp_status_string(int32_t status);

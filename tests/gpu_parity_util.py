@@ -29,11 +29,11 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0):
+def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0, head_lists=False):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
     db = upload(w, "cuda")
-    pipe = Pipeline(db, attn_splits=attn_splits)
+    pipe = Pipeline(db, attn_splits=attn_splits, head_lists=head_lists)
     pipe.run(alpha, sinks, local, correction)
     torch.cuda.synchronize()
     rp, ci = pipe.csr()
@@ -51,10 +51,12 @@ def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0):
 
 
 def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
-            check_pool=True):
-    """Compare GPU results `g` with the oracle on `rows` ((h, s, I) triples;
-    default all).  Returns a stats dict; raises AssertionError on failure."""
+            check_pool=True, head_lists=False):
+    """Compare GPU results `g` with the oracle on `rows` ((owner, s, I)
+    triples; default all; the owner is the KV head, or the query head with
+    head_lists).  Returns a stats dict; raises AssertionError on failure."""
     prob = OracleProblem.from_workload(w)
+    prob.head_lists = head_lists
     spec = w.spec
     qoff = prob.query_block_offsets()
     t0 = time.time()
@@ -72,8 +74,8 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
     assert np.all(np.isfinite(g["out"])), "non-finite output"
     assert np.all(np.isfinite(g["lse"])), "non-finite lse"
     stats = dict(rows=len(res), band=0, mismatch=0, score_err=0.0, out_err=0.0, lse_err=0.0)
-    G = spec.group
     for (h, s, I), r in res.items():
+        heads = prob.list_heads(h)
         row = prob.row_index(h, s, I)
         i0 = prob.ctx(s) // spec.block_size
         # pooled scores (fast path)
@@ -92,9 +94,9 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
         cu0 = int(w.cu_seqlens[s])
         nI = r["out"].shape[1]
         toks = cu0 + I * spec.block_size - prob.ctx(s) + np.arange(nI)
-        og = g["out"][toks][:, h * G:(h + 1) * G, :].transpose(1, 0, 2)
+        og = g["out"][toks][:, heads, :].transpose(1, 0, 2)
         stats["out_err"] = max(stats["out_err"], float(np.max(np.abs(og - r["out"]))))
-        lg = g["lse"][h * G:(h + 1) * G][:, toks]
+        lg = g["lse"][heads][:, toks]
         stats["lse_err"] = max(stats["lse_err"], float(np.max(np.abs(lg - r["lse"]))))
     stats["oracle_s"] = time.time() - t0
     log(f"  parity {spec.name}: {stats}")
@@ -105,17 +107,18 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
     return stats
 
 
-def sample_rows(w, n_per_head, seed=0):
-    """Seeded sample of (h, s, I) rows, always including each sequence's
+def sample_rows(w, n_per_head, seed=0, head_lists=False):
+    """Seeded sample of (owner, s, I) rows, always including each sequence's
     first and last query block."""
     rng = np.random.default_rng(seed)
     prob = OracleProblem.from_workload(w)
+    prob.head_lists = head_lists
     rows = []
     for s in range(prob.num_seqs):
         qb = list(prob.query_blocks(s))
         if not qb:
             continue
-        for h in range(prob.hkv):
+        for h in range(prob.list_owners):
             pick = set([qb[0], qb[-1]])
             pick |= set(int(x) for x in rng.choice(qb, size=min(len(qb), n_per_head), replace=False))
             rows += [(h, s, I) for I in sorted(pick)]

@@ -136,3 +136,22 @@ def test_attn_split_workspace_and_validation(bind):
     assert w0 > w1
     with pytest.raises(bind.FpError):
         _ = _problem(bind, attn_splits=-1).num_blocks
+
+
+def test_size_queries_per_query_head_lists(bind):
+    """head_lists = 1: one index list per query head, so the score and CSR
+    rows (and the CSR capacity) scale with Hq instead of Hkv; pooled rows and
+    workspaces for pooling stay per KV head."""
+    n = [3, 2, 1, 8]
+    base = _problem(bind, seqlens=(300, 129, 1, 1000))
+    per = _problem(bind, seqlens=(300, 129, 1, 1000), head_lists=True)
+    assert per.list_owners == 8 and base.list_owners == 2
+    assert per.num_blocks == base.num_blocks == sum(n)
+    assert per.num_rows == 8 * sum(n)
+    assert per.scores_elems == 8 * sum(n) * 8
+    assert per.csr_capacity == 4 * base.csr_capacity
+    assert per.workspace_bytes(bind.FP_WS_SELECT) > base.workspace_bytes(bind.FP_WS_SELECT)
+    bad = _problem(bind)
+    bad.c.head_lists = 2
+    with pytest.raises(bind.FpError, match="head_lists"):
+        bad.num_rows

@@ -300,3 +300,56 @@ def test_ranked_selection_parity(mode, param):
         wl = max(wl, float(np.abs(lse[h * G:(h + 1) * G][:, toks] - r["lse"]).max()))
     log(f"  out err {worst:.3g} lse err {wl:.3g}")
     assert worst <= 2e-2 and wl <= 5e-2
+
+
+HEAD_LIST_CASES = [
+    # name, spec kwargs, cached prefix per sequence (None: whole prompts)
+    ("heads_bf16_ragged_g4", dict(seqlens=(300, 129, 1, 1000), num_q_heads=8, num_kv_heads=2,
+                                  page_size=16, paging="permute", seed=150), None),
+    ("heads_e4m3_g8", dict(seqlens=(1100, 260), num_q_heads=8, num_kv_heads=1, qk_dtype="e4m3",
+                           v_dtype="bf16", page_size=16, paging="roundrobin", seed=151), None),
+    ("heads_bf16_chunk", dict(seqlens=(700, 1000), num_q_heads=8, num_kv_heads=2, page_size=64,
+                              seed=152), (256, 896)),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 0], ids=["nosplit", "autosplit"])
+@pytest.mark.parametrize("name,kw,ctx", HEAD_LIST_CASES, ids=[c[0] for c in HEAD_LIST_CASES])
+def test_per_query_head_lists_parity(name, kw, ctx, splits):
+    """One index list per query head (head_lists): scores, lists, outputs
+    and lse of every (query head, sequence, query block) row against the
+    oracle's per-head reading."""
+    log(f"case {name} splits={splits}")
+    w = make_workload(custom_spec(name=name, **kw))
+    if ctx is not None:
+        w = chunk_view(w, ctx)
+    g = run_gpu(w, 0.1, attn_splits=splits, head_lists=True)
+    assert g["scores"].shape[0] == w.spec.num_q_heads
+    compare(w, g, 0.1, head_lists=True)
+
+
+def test_per_query_head_lists_gqa_32k_sampled():
+    """32K prompt, Hq=32 / Hkv=4, per-query-head lists on sampled rows."""
+    log("case gqa_32k head_lists")
+    w = make_workload(spec_for("gqa_32k"))
+    g = run_gpu(w, 0.1, head_lists=True)
+    compare(w, g, 0.1, rows=sample_rows(w, 2, head_lists=True), check_pool=False,
+            head_lists=True)
+
+
+def test_per_query_head_lists_group_of_one_is_the_group_path():
+    """With one query head per KV head the two list readings are the same
+    computation: bit-identical scores, lists, outputs and lse."""
+    log("case heads_g1")
+    w = make_workload(custom_spec(name="heads_g1", seqlens=(900, 300), num_q_heads=2,
+                                  num_kv_heads=2, page_size=32, seed=153))
+    a = run_gpu(w, 0.1, attn_splits=1)
+    b = run_gpu(w, 0.1, attn_splits=1, head_lists=True)
+    for k in ("row_ptr", "col_idx", "out", "lse"):
+        assert np.array_equal(a[k], b[k]), k
+    # scores: only the causal entries J <= I are written
+    qoff = np.concatenate([[0], np.cumsum([-(-n // 128) for n in w.spec.seqlens])])
+    for s_ in range(len(w.spec.seqlens)):
+        for I in range(int(qoff[s_ + 1] - qoff[s_])):
+            r = int(qoff[s_]) + I
+            assert np.array_equal(a["scores"][:, r, :I + 1], b["scores"][:, r, :I + 1]), (s_, I)
