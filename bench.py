@@ -99,19 +99,22 @@ def causal_blocks(seqlens, hkv, B=128, ctx=None):
     return hkv * tot
 
 
-def kept_pairs(row_ptr, col_idx, spec, ctx=None):
+def kept_pairs(row_ptr, col_idx, spec, ctx=None, head_lists=False):
     """Kept query-key pairs summed over query heads, and the mean-correction
     (query row, pruned block) pairs, from the CSR lists (host arithmetic on
     the index lists, for reporting only).  ctx: cached prefix per sequence
-    (chunked prefill; rows cover the query blocks only)."""
-    B, g = spec.block_size, spec.group
+    (chunked prefill; rows cover the query blocks only).  head_lists: one
+    list per query head (rows per query head, each used by one head)."""
+    B = spec.block_size
+    g = 1 if head_lists else spec.group
+    owners = spec.num_q_heads if head_lists else spec.num_kv_heads
     ctx = ctx or [0] * len(spec.seqlens)
     nq = [-(-L // B) - c // B for L, c in zip(spec.seqlens, ctx)]
     qoff = np.concatenate([[0], np.cumsum(nq)])
     nrow = int(qoff[-1])
     kept = 0
     corr = 0
-    for h in range(spec.num_kv_heads):
+    for h in range(owners):
         for s, L in enumerate(spec.seqlens):
             n, i0 = -(-L // B), ctx[s] // B
             cnt = np.minimum(B, L - np.arange(n) * B)
@@ -125,7 +128,7 @@ def kept_pairs(row_ptr, col_idx, spec, ctx=None):
     return kept * g, corr * g
 
 
-def gpu_setup(spec, threads=None, ctx=None, attn_splits=0):
+def gpu_setup(spec, threads=None, ctx=None, attn_splits=0, head_lists=False):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
     from synthetic import chunk_view, make_workload
@@ -135,7 +138,7 @@ def gpu_setup(spec, threads=None, ctx=None, attn_splits=0):
         w = chunk_view(w, ctx)
     t_gen = time.time() - t0
     db = upload(w, "cuda")
-    pipe = Pipeline(db, attn_splits=attn_splits)
+    pipe = Pipeline(db, attn_splits=attn_splits, head_lists=head_lists)
     torch.cuda.synchronize()
     return w, pipe, t_gen
 
@@ -243,6 +246,8 @@ def main():
     ap.add_argument("--chunk-ctx", type=int, default=None, metavar="TOKENS",
                     help="chunked prefill: the first TOKENS tokens of every prompt are already "
                          "cached (a multiple of 128); the step processes the rest")
+    ap.add_argument("--head-lists", action="store_true",
+                    help="one index list per query head instead of per KV group (ablation)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration)")
@@ -266,7 +271,8 @@ def main():
     correction = not args.no_correction
     ctx = None if args.chunk_ctx is None else [min(args.chunk_ctx, L) // 128 * 128
                                                for L in spec.seqlens]
-    w, pipe, t_gen = gpu_setup(spec, ctx=ctx, attn_splits=args.attn_splits)
+    hl = args.head_lists
+    w, pipe, t_gen = gpu_setup(spec, ctx=ctx, attn_splits=args.attn_splits, head_lists=hl)
     print(f"# generated {spec.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
     select = None
     if args.select != "threshold":
@@ -275,7 +281,7 @@ def main():
         select = (mode, float(val))
     t = time_steps(pipe, args.alpha, correction, args.steps, args.warmup, select=select)
     rp, ci = pipe.csr()
-    kp, cp = kept_pairs(rp, ci, spec, ctx)
+    kp, cp = kept_pairs(rp, ci, spec, ctx, hl)
     d = spec.head_dim
     eff = 4 * d * kp / (t["step_ms"] * 1e-3) / 1e12
     attn_flop = 4 * d * (kp + (cp if correction else 0))
@@ -283,7 +289,7 @@ def main():
     peak = attn_peak(spec, kp, cp, correction)
     causal = causal_pairs(spec.seqlens, ctx=ctx) * spec.num_q_heads
     nrows = int(rp.shape[0] - 1)
-    cblocks = causal_blocks(spec.seqlens, spec.num_kv_heads, ctx=ctx)
+    cblocks = causal_blocks(spec.seqlens, spec.num_q_heads if hl else spec.num_kv_heads, ctx=ctx)
     line = {
         "metric": "sparse prefill attn ms + effective TFLOP/s (% MFMA peak) at 128K, bf16/fp8",
         "value": round(eff, 3),
@@ -340,6 +346,9 @@ def main():
     if select is not None:
         line["config"]["select"] = args.select
         line["roofline"]["traffic"] = None
+    if hl:
+        line["config"]["index_lists"] = "per_query_head"
+        line["roofline"]["traffic"] = None
     if ctx is not None:
         line["config"]["chunk"] = {"cached_tokens": ctx, "query_tokens":
                                    [L - c for L, c in zip(spec.seqlens, ctx)]}
@@ -351,14 +360,14 @@ def main():
                 for corr in (True, False):
                     ts = time_steps(pipe, a, corr, max(3, args.steps // 2), 1)
                     r2, c2 = pipe.csr()
-                    k2, q2 = kept_pairs(r2, c2, spec, ctx)
+                    k2, q2 = kept_pairs(r2, c2, spec, ctx, hl)
                     rec = dict(workload=spec.name, alpha=a, correction=corr,
                                block_density=int(r2[-1]) / cblocks,
                                pair_density=k2 / causal,
                                eff_tflops=4 * d * k2 / (ts["step_ms"] * 1e-3) / 1e12, **ts)
                     f.write(json.dumps(rec) + "\n")
                     print("# sweep " + json.dumps(rec), file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline and ctx is None and select is None:
+    if not args.no_cpu_baseline and ctx is None and select is None and not hl:
         line["cpu_baseline"] = cpu_baseline(w, args.alpha, correction, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)
 
