@@ -63,14 +63,36 @@ __global__ __launch_bounds__(256) void pool_kernel(
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int t = tl; t < nJ; t += 16) {
-    const int p = p0 + t;
-    const int page = page_table[(int64_t)s * max_pages + p / page_size];
-    const int64_t elem = (((int64_t)page * page_size + p % page_size) * hkv + h) * kHeadDim + chunk * 8;
-    float v[8];
-    if (is_v) load8<VDT>(v_cache, elem, v); else load8<KDT>(k_cache, elem, v);
+  const int32_t* prow = page_table + (int64_t)s * max_pages;
+  auto row_elem = [&](int p, int page) {
+    return (((int64_t)page * page_size + p % page_size) * hkv + h) * kHeadDim + chunk * 8;
+  };
+  if (nJ == kBlock) {
+    // whole block: all eight page lookups, then all eight row loads in
+    // flight at once (one at a time leaves HBM half idle); same summation
+    // order as the general loop below
+    int page[kBlock / 16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int it = 0; it < kBlock / 16; ++it) page[it] = prow[(p0 + tl + 16 * it) / page_size];
+    float v[kBlock / 16][8];
+#pragma unroll
+    for (int it = 0; it < kBlock / 16; ++it) {
+      const int64_t elem = row_elem(p0 + tl + 16 * it, page[it]);
+      if (is_v) load8<VDT>(v_cache, elem, v[it]); else load8<KDT>(k_cache, elem, v[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < kBlock / 16; ++it)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[it][i];
+  } else {
+    for (int t = tl; t < nJ; t += 16) {
+      const int p = p0 + t;
+      float v[8];
+      const int64_t elem = row_elem(p, prow[p / page_size]);
+      if (is_v) load8<VDT>(v_cache, elem, v); else load8<KDT>(k_cache, elem, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[tl][chunk * 8 + i] = acc[i];
