@@ -154,10 +154,12 @@ const char* fp_last_error(void);
  * sequence s for KV head h (n_J = tokens actually in the block); v_mean the
  * same for values.
  *
- * Scores (same summary, 3.1 query pooling + global re-weighting): for KV head
- * h and query block I, let rows(I) be every (query head of h's group, query
- * token of block I) and x_rJ = softmax_scale * q_r . kbar_J for J <= I (key
- * blocks of the cached prefix included).  Then
+ * Scores (same summary, 3.1 query pooling + global re-weighting): for list
+ * owner h (KV head h; with head_lists, query head h) and query block I, let
+ * rows(I) be every (query head of h's group, or query head h alone with
+ * head_lists; query token of block I) and x_rJ = softmax_scale * q_r . kbar_J
+ * for J <= I, kbar of the owner's KV head (key blocks of the cached prefix
+ * included).  Then
  *     block_scores[h][qboff_s + I - c_s/128][J] = M_IJ + ln S_IJ,
  *     M_IJ = max_r x_rJ,  S_IJ = sum_r exp(x_rJ - M_IJ),
  * the log of the max-normalised exp-sum.  Re-weighting a row against its top
@@ -237,7 +239,8 @@ int fp_select_topp(const fp_problem* p, const float* block_scores, float top_p,
  *
  * For query head hq, query token at position p (counted from the start of
  * the sequence, cached prefix included) of block I of sequence s, and the
- * list K(h, s, I) = col_idx[row_ptr[r] .. row_ptr[r+1]) of row r = (h, s, I):
+ * list K(h, s, I) = col_idx[row_ptr[r] .. row_ptr[r+1]) of row r = (h, s, I),
+ * h = hq / (Hq / Hkv) its KV head, or h = hq with head_lists:
  *   E = { tokens j <= p of the listed blocks },  y_j = softmax_scale * q . k_j
  *   C = { J <= I not listed } if mean_correction, else empty,
  *       z_J = softmax_scale * q . kbar_J + ln n_J,  value vbar_J
