@@ -182,6 +182,26 @@ def time_steps(pipe, alpha, correction, steps, warmup, sinks=256, local=512, sel
     return dict(wall_ms=wall, step_ms=tot, discover_ms=disc, select_ms=sel, attn_ms=att)
 
 
+def time_graph(pipe, alpha, correction, steps, warmup, sinks=256, local=512):
+    """Whole steps replayed from one HIP graph (captured after an eager step):
+    mean replay time (events) and host wall time per step."""
+    import torch
+    graph = pipe.graph(alpha, sinks, local, correction)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        graph.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    return dict(step_ms=e0.elapsed_time(e1) / steps, wall_ms=wall)
+
+
 def cpu_baseline(w, alpha, correction, budget_s=20.0, seed=0):
     """Time the fp64 oracle on a seeded sample of (kv head, query block) rows
     of the same workload, growing the sample until ~budget_s of CPU work."""
@@ -248,6 +268,8 @@ def main():
                          "cached (a multiple of 128); the step processes the rest")
     ap.add_argument("--head-lists", action="store_true",
                     help="one index list per query head instead of per KV group (ablation)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time whole steps replayed from one HIP graph (graph_ms_per_step)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration)")
@@ -346,6 +368,10 @@ def main():
     if select is not None:
         line["config"]["select"] = args.select
         line["roofline"]["traffic"] = None
+    if args.graph and select is None:
+        tg = time_graph(pipe, args.alpha, correction, args.steps, args.warmup)
+        line["graph_ms_per_step"] = round(tg["step_ms"], 4)
+        line["graph_wall_ms_per_step"] = round(tg["wall_ms"], 4)
     if hl:
         line["config"]["index_lists"] = "per_query_head"
         line["roofline"]["traffic"] = None

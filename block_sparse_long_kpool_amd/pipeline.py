@@ -123,6 +123,23 @@ class Pipeline:
         self.attend(correction, True, stream)
         return self.out
 
+    def graph(self, alpha: float, sink_tokens: int = 256, local_tokens: int = 512,
+              correction: bool = True):
+        """Capture one whole step (discover, select, attention) into a HIP graph
+        on this pipeline's buffers and return it (a torch.cuda.CUDAGraph).  A
+        replay recomputes everything from the current contents of the input
+        tensors, so new inputs of the same shape are copied into them in place.
+        One eager step runs first: kernel attributes are set on a kernel's
+        first launch, which must not happen inside the capture.  The library
+        records no memset or allocation, only kernel launches."""
+        import torch
+        self.run(alpha, sink_tokens, local_tokens, correction)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run(alpha, sink_tokens, local_tokens, correction)
+        return g
+
     def csr(self):
         """(row_ptr, col_idx) on the host as numpy int64 arrays."""
         rp = self.row_ptr.cpu().numpy().astype("int64")
