@@ -103,7 +103,7 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   return FP_OK;
 }
 
-struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; };
+struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; float* kres; };
 struct SelectWs { int32_t* kboff; int32_t* qboff; uint32_t* bits; int32_t* counts; };
 struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; float* opart; float* lpart; };
 
@@ -131,7 +131,8 @@ size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
     DiscoverWs w;
     w.kboff = (int32_t*)take(boff_bytes);
     w.qboff = (int32_t*)take(boff_bytes);
-    w.km16 = (u16*)take(2 * pooled16);  // hi part, then lo part
+    w.km16 = (u16*)take(pooled16);  // kbar rounded to bf16
+    w.kres = (float*)take(sizeof(float) * (size_t)g.hkv * (size_t)g.num_blocks);
     if (out) *reinterpret_cast<DiscoverWs*>(out) = w;
   } else if (which == FP_WS_SELECT) {
     SelectWs w;
@@ -202,7 +203,8 @@ int64_t fp_num_rows(const fp_problem* p) {
 
 int64_t fp_scores_elems(const fp_problem* p) {
   Geometry g;
-  return make_geometry(p, &g) == FP_OK ? g.num_rows * (int64_t)g.max_blocks : -1;
+  // the scores, then one error bound per score row
+  return make_geometry(p, &g) == FP_OK ? g.num_rows * ((int64_t)g.max_blocks + 1) : -1;
 }
 
 int64_t fp_csr_capacity(const fp_problem* p) {
@@ -253,9 +255,10 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const v
   const SeqMap m = seq_map(p, w.kboff, w.qboff);
   if ((st = hip_status(launch_plan(m, s), "plan"))) return st;
   if ((st = hip_status(launch_pool(g, m, p->page_table_dev, k_cache, v_cache, p->k_scale_dev,
-                                   k_mean, v_mean, w.km16, s), "pool")))
+                                   k_mean, v_mean, w.km16, w.kres, s), "pool")))
     return st;
-  return hip_status(launch_scores(g, m, q, p->q_scale_dev, w.km16, block_scores, s), "scores");
+  return hip_status(launch_scores(g, m, q, p->q_scale_dev, w.km16, w.kres, block_scores, s),
+                    "scores");
 }
 
 int fp_select(const fp_problem* p, const void* q, const float* k_mean, const float* block_scores,

@@ -244,12 +244,19 @@ __device__ __forceinline__ void interleave() {
 // Block offsets kboff / qboff of the map (one workgroup).
 hipError_t launch_plan(const SeqMap& m, hipStream_t st);
 
+// Pooling also writes kbar rounded to bf16 and, per key block, the bound
+// kres_J = |kbar_J - bf16(kbar_J)|_2 + 2^-17 |bf16(kbar_J)|_2 on how far a
+// query row of unit norm can move its bf16 dot product with kbar_J (rounding
+// of kbar, plus fp32 accumulation of 128 exact products).
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
-                       float* k_mean, float* v_mean, u16* k_mean_bf16, hipStream_t st);
+                       float* k_mean, float* v_mean, u16* k_mean_bf16, float* kres,
+                       hipStream_t st);
 
+// Scores [lists * NQ, max_blocks] followed by one error bound per score row.
 hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
-                         const u16* k_mean_bf16, float* scores, hipStream_t st);
+                         const u16* k_mean_bf16, const float* kres, float* scores,
+                         hipStream_t st);
 
 hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
                          const float* k_mean, const float* scores, float alpha, int n_sink,

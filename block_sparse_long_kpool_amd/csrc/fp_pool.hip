@@ -48,8 +48,9 @@ __global__ __launch_bounds__(256) void pool_kernel(
     SeqMap m, const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
     int64_t num_blocks, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ k_scale, float* __restrict__ k_mean, float* __restrict__ v_mean,
-    u16* __restrict__ k_mean_bf16) {
+    u16* __restrict__ k_mean_bf16, float* __restrict__ kres) {
   __shared__ float red[16][kHeadDim + 4];
+  __shared__ float2 nred[kHeadDim / 64];
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z == 1;
@@ -108,25 +109,37 @@ __global__ __launch_bounds__(256) void pool_kernel(
     if (is_v) {
       v_mean[o] = mean;
     } else {
-      // two-term bf16 split (hi + lo) of the fp32 mean for the discovery MFMA
+      // the fp32 mean rounded to bf16 for the discovery MFMA
       k_mean[o] = mean;
       const __bf16 hi = f32_to_bf16(mean);
-      const __bf16 lo = f32_to_bf16(mean - (float)hi);
-      const int64_t nel = (int64_t)hkv * num_blocks * kHeadDim;
       k_mean_bf16[o] = __builtin_bit_cast(u16, hi);
-      k_mean_bf16[nel + o] = __builtin_bit_cast(u16, lo);
+      // squared norms of the rounding residual (exact: hi is within a bf16
+      // half-ulp of mean) and of hi, summed over the 128 dims (two waves)
+      const float r = mean - (float)hi;
+      const float hf = (float)hi;
+      const float r2 = wave_sum(r * r), h2 = wave_sum(hf * hf);
+      if ((d & 63) == 0) nred[d >> 6] = make_float2(r2, h2);
+    }
+  }
+  if (!is_v) {  // uniform per workgroup
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float r2 = nred[0].x + nred[1].x, h2 = nred[0].y + nred[1].y;
+      // the factor covers the fp32 rounding of the sums and square roots
+      kres[(int64_t)h * num_blocks + gb] = (__fsqrt_rn(r2) + 0x1p-17f * __fsqrt_rn(h2)) * (1.f + 0x1p-12f);
     }
   }
 }
 
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
-                       float* k_mean, float* v_mean, u16* k_mean_bf16, hipStream_t st) {
+                       float* k_mean, float* v_mean, u16* k_mean_bf16, float* kres,
+                       hipStream_t st) {
   dim3 grid((unsigned)g.num_blocks, (unsigned)g.hkv, 2);
 #define FP_POOL(KD, VD)                                                                       \
   hipLaunchKernelGGL((pool_kernel<KD, VD>), grid, dim3(256), 0, st, m, page_table,            \
                      g.max_pages, g.page_size, g.hkv, g.num_blocks, k_cache,                   \
-                     v_cache, k_scale, k_mean, v_mean, k_mean_bf16)
+                     v_cache, k_scale, k_mean, v_mean, k_mean_bf16, kres)
   if (g.qk_dtype == FP_BF16 && g.v_dtype == FP_BF16) FP_POOL(FP_BF16, FP_BF16);
   else if (g.qk_dtype == FP_E4M3 && g.v_dtype == FP_BF16) FP_POOL(FP_E4M3, FP_BF16);
   else if (g.qk_dtype == FP_F32 && g.v_dtype == FP_F32) FP_POOL(FP_F32, FP_F32);

@@ -15,16 +15,22 @@
 //     in passes of 8 waves x 2 chunks x 32 rows, each wave holding the Q
 //     fragments of its two chunks in registers for the whole pass, so Q is
 //     read from HBM once (passes = g / 4).
-//   * pooled keys (bf16 hi and lo terms of kbar, L2-resident) stream through
+//   * pooled keys (kbar rounded to bf16, L2-resident) stream through
 //     double-buffered LDS in tiles of 128 keys, copied with
 //     global_load_lds_dwordx4 (no staging registers) into XOR-swizzled 256-B
 //     rows, so the MFMA operand reads are conflict-free.
-//   * X = Q . Kbar^T on v_mfma_f32_32x32x16_bf16, hi and lo terms into one
-//     fp32 accumulator (relative residual of the split ~2^-17, so the fast
-//     logits carry errors of a few 1e-5 only).  In the result layout a lane
-//     owns one pooled-key column and 16 rows of each chunk: the column max and
-//     exp-sum are lane-local, lanes l and l^32 are merged with one
-//     v_permlane32_swap each, and the 8 waves through LDS once per tile.
+//   * X = Q . Kbar^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  In
+//     the result layout a lane owns one pooled-key column and 16 rows of each
+//     chunk: the column max and exp-sum are lane-local, lanes l and l^32 are
+//     merged with one v_permlane32_swap each, and the 8 waves through LDS
+//     once per tile.
+//   * error bound instead of a second MFMA term: rounding kbar_J to bf16
+//     moves x_rJ by at most softmax_scale * |q_r|_2 * |kbar_J - bf16(kbar_J)|_2
+//     (Cauchy-Schwarz), and a log-sum-exp over rows moves by at most the
+//     largest such shift.  The kernel writes that bound per score row
+//     (largest query-row norm of the row times the largest residual bound of
+//     its key blocks, from the pooling pass); the selection re-evaluates in
+//     float64 every entry the bound cannot decide.
 //   * software pipeline inside a wave: the MFMAs of key chunk j+1 (second
 //     accumulator set) are independent of the max / exp / sum of chunk j, so
 //     the matrix core and the VALU overlap; the logit scale is folded into one
@@ -47,8 +53,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct ScoresSmem {
-  u16 kb[2][2][kTerm];           // [buffer][hi, lo]: 128 KiB
+  u16 kb[2][kTerm];              // [buffer]: 64 KiB
   float2 part[2][kWaves][kJT];   // per wave (max, sum) of each key, by buffer
+  float red[2][kWaves];          // per wave: largest residual bound, largest row norm^2
 };
 constexpr size_t kScoresSmem = sizeof(ScoresSmem);
 
@@ -56,8 +63,10 @@ struct ScoresArgs {
   SeqMap m;
   const void* q;
   const float* q_scale;
-  const u16* kmean16;
+  const u16* kmean16;   // kbar rounded to bf16 [Hkv, NK, 128]
+  const float* kres;    // residual bound of each pooled key [Hkv, NK]
   float* scores;
+  float* errb;          // per score row: bound on the error of its entries
   int64_t num_blocks;   // NK (pooled rows per KV head)
   int64_t num_qblocks;  // NQ (score rows per KV head)
   int hq, hkv, group, max_blocks;  // group: query heads per index list (1 per query head)
@@ -104,23 +113,19 @@ __device__ __forceinline__ void load_q_frag(const void* q, int64_t row_elem, boo
 }
 
 // X chunk of 32 pooled keys (rows jc*32 .. +31 of the LDS tile) against the
-// wave's kRC row chunks: 8 head-dim steps x (hi, lo).  Chunks without valid
+// wave's kRC row chunks: 8 head-dim steps.  Chunks without valid
 // rows hold zero Q fragments and are computed anyway (their results are
 // masked), which keeps the instruction stream branch-free.
-__device__ __forceinline__ void mma_chunk(const u16* bh, const u16* bl, int jc, int col, int half,
+__device__ __forceinline__ void mma_chunk(const u16* bh, int jc, int col, int half,
                                           const bf16x8 (&qf)[kRC][8], f32x16* acc) {
   const int r = jc * 32 + col;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const int off = r * kHeadDim + swz16(8 * half + kk, r) * 8;
     const bf16x8 vh = *reinterpret_cast<const bf16x8*>(bh + off);
-    const bf16x8 vl = *reinterpret_cast<const bf16x8*>(bl + off);
 #pragma unroll
     for (int rc = 0; rc < kRC; ++rc)
       acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], vh, kk ? acc[rc] : f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int rc = 0; rc < kRC; ++rc)
-      acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], vl, acc[rc], 0, 0, 0);
   }
 }
 
@@ -156,26 +161,94 @@ __device__ __forceinline__ float2 column_stats(const f32x16* acc, const float* c
   return make_float2(m, pair_sum(s));
 }
 
+// Slice KK (0..7) of the column statistics of one finished 32-key chunk,
+// spread over the eight head-dim steps of the next chunk's MFMAs: slices 0-1
+// take the column max of row chunk 0 and 1 (then the lane-pair max), slices
+// 2-7 the exp-sum of the 32 (row chunk, row) elements in order, so the
+// operations and the summation order are those of column_stats.
+template <bool MASKED, int KK>
+__device__ __forceinline__ void stats_slice(const f32x16* acc, const float* csc, const int* nval,
+                                            int half, float& m, float& s) {
+  if constexpr (KK < 2) {
+    constexpr int rc = KK;
+    float mr = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      mr = fmaxf(mr, (!MASKED || row < nval[rc]) ? acc[rc][i] : -INFINITY);
+    }
+    if constexpr (KK == 0) {
+      m = fmaxf(-INFINITY, mr * csc[0]);
+      s = 0.f;
+    } else {
+      m = pair_max(fmaxf(m, mr * csc[1]));
+    }
+  } else {
+    constexpr int e0 = KK == 2 ? 0 : KK == 3 ? 5 : KK == 4 ? 10 : KK == 5 ? 15 : KK == 6 ? 20 : 26;
+    constexpr int e1 = KK == 7 ? 32 : (KK == 6 ? 26 : e0 + 5);
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const int rc = e >> 4, i = e & 15;
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      const float x = __builtin_amdgcn_exp2f(fmaf(acc[rc][i], csc[rc], -m));
+      s += (!MASKED || row < nval[rc]) ? x : 0.f;
+    }
+  }
+}
+
+// MFMAs of head-dim step kk of one 32-key chunk.
+__device__ __forceinline__ void mma_step(const bf16x8 (&qf)[kRC][8], int kk, bf16x8 vh,
+                                         f32x16* acc) {
+#pragma unroll
+  for (int rc = 0; rc < kRC; ++rc)
+    acc[rc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rc][kk], vh, kk ? acc[rc] : f32x16{}, 0, 0, 0);
+}
+
+// One 32-key chunk's MFMAs with the statistics of the previous chunk woven
+// in: per head-dim step, the operand of the next step is read from LDS, the
+// two MFMAs issue one by one, each followed by a share of the statistics
+// (independent VALU work that the in-order wave issues while the matrix core
+// runs).  Scheduling fences between steps keep this order.
+template <bool MASKED>
+__device__ __forceinline__ float2 chunk_overlapped(const u16* bh, int jc, int col,
+                                                   int half, const bf16x8 (&qf)[kRC][8],
+                                                   f32x16* acc, const f32x16* prev,
+                                                   const float* csc, const int* nval) {
+  const int r = jc * 32 + col;
+  auto opnd = [&](const u16* b, int kk) {
+    return *reinterpret_cast<const bf16x8*>(b + r * kHeadDim + swz16(8 * half + kk, r) * 8);
+  };
+  float m, s;
+  bf16x8 vh = opnd(bh, 0);
+#define FP_STEP(KK)                                       \
+  {                                                       \
+    bf16x8 nh;                                            \
+    if constexpr (KK < 7) nh = opnd(bh, KK + 1);          \
+    mma_step(qf, KK, vh, acc);                            \
+    stats_slice<MASKED, KK>(prev, csc, nval, half, m, s); \
+    interleave<2, 1>();                                   \
+    __builtin_amdgcn_sched_barrier(0);                    \
+    if constexpr (KK < 7) vh = nh;                        \
+  }
+  FP_STEP(0) FP_STEP(1) FP_STEP(2) FP_STEP(3) FP_STEP(4) FP_STEP(5) FP_STEP(6) FP_STEP(7)
+#undef FP_STEP
+  return make_float2(m, pair_sum(s));
+}
+
 // One LDS tile for this wave.  Full tiles (kJC chunks) run as one basic block
 // with two accumulator sets: chunk j+1's MFMAs overlap chunk j's statistics.
 template <bool MASKED>
-__device__ __forceinline__ void tile_chunks(const u16* bh, const u16* bl, int njc, int col,
+__device__ __forceinline__ void tile_chunks(const u16* bh, int njc, int col,
                                             int half, const bf16x8 (&qf)[kRC][8],
                                             const float* csc, const int* nval, float2* part) {
   f32x16 acc0[kRC], acc1[kRC];
   if (njc == kJC) {
     static_assert(kJC == 4, "pipeline below is written for 4 chunks per tile");
-    mma_chunk(bh, bl, 0, col, half, qf, acc0);
+    mma_chunk(bh, 0, col, half, qf, acc0);
     __builtin_amdgcn_sched_barrier(0);
-    mma_chunk(bh, bl, 1, col, half, qf, acc1);
-    const float2 s0 = column_stats<MASKED>(acc0, csc, nval, half);
-    interleave<16 * kRC, 16>();
-    mma_chunk(bh, bl, 2, col, half, qf, acc0);
-    const float2 s1 = column_stats<MASKED>(acc1, csc, nval, half);
-    interleave<16 * kRC, 16>();
-    mma_chunk(bh, bl, 3, col, half, qf, acc1);
-    const float2 s2 = column_stats<MASKED>(acc0, csc, nval, half);
-    interleave<16 * kRC, 16>();
+    const float2 s0 = chunk_overlapped<MASKED>(bh, 1, col, half, qf, acc1, acc0, csc, nval);
+    const float2 s1 = chunk_overlapped<MASKED>(bh, 2, col, half, qf, acc0, acc1, csc, nval);
+    const float2 s2 = chunk_overlapped<MASKED>(bh, 3, col, half, qf, acc1, acc0, csc, nval);
     const float2 s3 = column_stats<MASKED>(acc1, csc, nval, half);
     if (half == 0) {
       part[col] = s0;
@@ -185,7 +258,7 @@ __device__ __forceinline__ void tile_chunks(const u16* bh, const u16* bl, int nj
     }
   } else {
     for (int jc = 0; jc < njc; ++jc) {
-      mma_chunk(bh, bl, jc, col, half, qf, acc0);
+      mma_chunk(bh, jc, col, half, qf, acc0);
       const float2 st = column_stats<MASKED>(acc0, csc, nval, half);
       if (half == 0) part[jc * 32 + col] = st;
     }
@@ -213,7 +286,6 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   const int nI = qb.nI;
   const int64_t tok0 = qb.tok0;
   const u16* kbase = a.kmean16 + ((int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0) * kHeadDim;
-  const int64_t lo_off = (int64_t)a.hkv * a.num_blocks * kHeadDim;  // lo part follows the hi part
   float* out_row = a.scores + ((int64_t)h * a.num_qblocks + gq) * a.max_blocks;
   const int ncols = I + 1;
   const int ntiles_row = (ncols + kJT - 1) / kJT;
@@ -222,27 +294,40 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   if (tile0 >= tile1) return;  // whole workgroup: no barrier is skipped by part of it
   const int nchunks = 4 * a.group;  // 32-row chunks: (head, 32-token slice)
 
-  // Tile t of both terms = 64 segments of 1 KiB (4 key rows each); wave w
-  // issues segments 8w .. 8w+7.  Lane i of a segment copies physical chunk
-  // i%16 of key row 4*seg + i/16, i.e. logical chunk swz16(i%16, row).  Key
-  // rows past the causal range re-read the last valid row (results unused).
+  // Tile t = 32 segments of 1 KiB (4 key rows each); wave w issues segments
+  // 4w .. 4w+3.  Lane i of a segment copies physical chunk i%16 of key row
+  // 4*seg + i/16, i.e. logical chunk swz16(i%16, row).  Key rows past the
+  // causal range re-read the last valid row (results unused).  The lane index
+  // is made opaque here so that the source addresses are recomputed per tile
+  // instead of being hoisted into live registers.
   auto stage = [&](int tile, int buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int seg = wave * 8 + it;
-      const int term = seg >> 5;
-      const int sub = seg & 31;
-      const int r = 4 * sub + (lane >> 4);
+    for (int it = 0; it < 4; ++it) {
+      const int seg = wave * 4 + it;
+      const int r = 4 * seg + (ln >> 4);
       const int J = min(tile * kJT + r, ncols - 1);
-      const u16* src = kbase + (term ? lo_off : 0) + (int64_t)J * kHeadDim + swz16(lane & 15, r) * 8;
-      load_lds16(src, &sm.kb[buf][term][sub * 512]);
+      const u16* src = kbase + (int64_t)J * kHeadDim + swz16(ln & 15, r) * 8;
+      load_lds16(src, &sm.kb[buf][seg * 512]);
     }
   };
+
+  // Largest residual bound of the row's key blocks (published by the first
+  // barrier of the pass loop).
+  {
+    const float* kres = a.kres + (int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0;
+    float dm = 0.f;
+    for (int J = (int)threadIdx.x; J < ncols; J += 64 * kWaves) dm = fmaxf(dm, kres[J]);
+    dm = wave_max(dm);
+    if (lane == 0) sm.red[0][wave] = dm;
+  }
+  float qn2 = 0.f;  // largest squared query-row norm (q_scale included), all passes
 
   for (int pass = 0; pass * kChunksPerPass < nchunks; ++pass) {
     // ---- Q fragments of this pass (read once) ----
     bf16x8 qf[kRC][8];
-    float csc[kRC];
+    float csc[kRC], qsf[kRC];
     int nval[kRC];
     bool masked = false;
 #pragma unroll
@@ -257,25 +342,44 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       const bool rvalid = col < nval[rc];
       const int64_t row_elem = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim;
       load_q_frag<QDT>(a.q, row_elem, rvalid, half, qf[rc]);
-      float sc = a.logit_scale * kLog2e;
-      if constexpr (QDT == FP_E4M3) sc *= a.q_scale[hq_idx];
-      csc[rc] = sc;
+      qsf[rc] = QDT == FP_E4M3 ? a.q_scale[hq_idx] : 1.f;
+      csc[rc] = a.logit_scale * kLog2e * qsf[rc];
+    }
+    {
+      // squared norms of this wave's rows (lanes l and l^32 hold the halves)
+      float wn = 0.f;
+#pragma unroll
+      for (int rc = 0; rc < kRC; ++rc) {
+        float n2 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = (float)qf[rc][kk][i];
+            n2 = fmaf(v, v, n2);
+          }
+        n2 = pair_sum(n2) * (qsf[rc] * qsf[rc]);
+        wn = fmaxf(wn, n2);
+      }
+      wn = wave_max(wn);
+      if (lane == 0) sm.red[1][wave] = wn;
     }
 
     stage(tile0, tile0 & 1);
     wait_vm();
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) qn2 = fmaxf(qn2, sm.red[1][w]);
 
     for (int tile = tile0; tile < tile1; ++tile) {
       const int buf = tile & 1;
       if (tile + 1 < tile1) stage(tile + 1, buf ^ 1);
       const int njc = min(kJC, (ncols - tile * kJT + 31) >> 5);
-      const u16* bh = sm.kb[buf][0];
-      const u16* bl = sm.kb[buf][1];
+      const u16* bh = sm.kb[buf];
       if (masked)
-        tile_chunks<true>(bh, bl, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
+        tile_chunks<true>(bh, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
       else
-        tile_chunks<false>(bh, bl, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
+        tile_chunks<false>(bh, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
 
       wait_vm();
       __syncthreads();
@@ -306,6 +410,16 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
     }
     __syncthreads();
   }
+  if (threadIdx.x == 0) {
+    // every entry of the row: |L_fast - L| <= softmax_scale * max_r |q_r| *
+    // max_J kres_J (+ the fp32 rounding of the statistics); the factor covers
+    // the rounding of the bound itself.  Workgroups sharing a row (cparts > 1)
+    // store the same value.
+    float dm = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) dm = fmaxf(dm, sm.red[0][w]);
+    a.errb[(int64_t)h * a.num_qblocks + gq] = a.logit_scale * __fsqrt_rn(qn2) * dm * (1.f + 0x1p-10f);
+  }
 }
 
 template <int QDT>
@@ -325,7 +439,8 @@ hipError_t launch_scores_t(const ScoresArgs& a, dim3 grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
-                         const u16* k_mean_bf16, float* scores, hipStream_t st) {
+                         const u16* k_mean_bf16, const float* kres, float* scores,
+                         hipStream_t st) {
   // A launch with at most 128 (kv head, query block) rows (small chunks)
   // splits each row's key tiles over floor(256 / rows) workgroups (at most
   // 16), so that every CU has work; whole prompts never split.
@@ -338,7 +453,9 @@ hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, cons
   a.q = q;
   a.q_scale = q_scale;
   a.kmean16 = k_mean_bf16;
+  a.kres = kres;
   a.scores = scores;
+  a.errb = scores + g.num_rows * (int64_t)g.max_blocks;
   a.num_blocks = g.num_blocks;
   a.num_qblocks = g.num_qblocks;
   a.hq = g.hq;

@@ -7,10 +7,10 @@
 // Three kernels:
 //   decide  one workgroup (4 waves) per CSR row: re-weight (subtract the row
 //           max of the log scores), threshold, forced blocks -> keep bitmask
-//           + count.  Entries whose fast (bf16) score lies within kGuard of
-//           the threshold are re-evaluated in float64 from q and k_mean by
-//           the whole workgroup, with the row maximum re-evaluated the same
-//           way, so that every decision matches exact arithmetic.
+//           + count.  Entries whose fast (bf16) score lies within the row's
+//           guard of the threshold are re-evaluated in float64 from q and
+//           k_mean by the whole workgroup, with the row maximum re-evaluated
+//           the same way, so that every decision matches exact arithmetic.
 //   scan    one workgroup: exclusive prefix sum of the counts -> row_ptr.
 //   compact one wave per row: wavefront ballot + popcount prefix writes the
 //           kept block indices in ascending order.
@@ -21,169 +21,142 @@ namespace fp {
 namespace {
 
 // Fast-path error budget (natural-log units).  The discovery logits use the
-// pooled keys split into two bf16 terms (hi + lo, relative residual ~2^-17)
-// with fp32 MFMA accumulation; on attention-scale logits (|x| ~ 25) that
-// leaves absolute errors of a few 1e-5.  Every entry whose fast score lies
-// within kGuard of the threshold (and every candidate within kGuard of the
-// row max) is re-evaluated in float64, so decisions outside that window have
-// a margin of ~50x the fast path's error.
+// pooled keys rounded to bf16; the scores pass bounds, per score row, how far
+// that rounding and the fp32 accumulation of the dot products can move any
+// entry (E, stored after the scores).  kGuard adds an allowance for the fp32
+// statistics (exp2 / log2 / sums, below 1e-4 on these scales).  An entry and
+// the row max can each be off by E + kGuard / 2, so every entry within
+// guard = 2 E + kGuard of the threshold (and every candidate within guard of
+// the row max) is re-evaluated in float64; all other decisions are certain.
 constexpr float kGuard = 2e-3f;
 constexpr int kRowsPerWg = 4;
 
-// Exact score of pooled key J for the rows of (h, block I):
-// ln sum_r exp(x_rJ - ref) + ref, all in float64 (q as stored, widened; fp32
-// q rounded to bf16 first, as everywhere on this path).  One wave; lane l
-// takes rows l, l + 64, ... and reads each row with 16-byte loads into four
-// independent accumulators.  kbar is wave-uniform.
+constexpr int kSelThreads = 256;
+constexpr int kBatch = 8;  // pooled keys evaluated exactly per pass over a row's queries
+
 __device__ __forceinline__ double bf16_lo(unsigned w) { return (double)__uint_as_float(w << 16); }
 __device__ __forceinline__ double bf16_hi(unsigned w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
 
+// Head-dim elements 8c .. 8c+7 of the query row starting at element e0, as
+// the values the path consumes (bf16 widened; e4m3 codes decoded, the head's
+// scale applied later; fp32 rounded to bf16 first, as everywhere on this
+// path), in float64.
 template <int QDT>
-__device__ double exact_score(const void* q, const float* q_scale, const float* kbar, int hq,
-                              int group, int h, int64_t tok0, int nI, double scale, double ref,
-                              int lane) {
-  const int R = group * nI;
-  double acc = 0.0;
-  for (int r = lane; r < R; r += 64) {
-    const int hh = r / nI;
-    const int t = r - hh * nI;
-    const int hq_idx = h * group + hh;
-    const int64_t e0 = ((tok0 + t) * hq + hq_idx) * (int64_t)kHeadDim;
-    double d[4] = {0.0, 0.0, 0.0, 0.0};
-    if constexpr (QDT == FP_BF16) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(q) + e0);
-#pragma unroll 4
-      for (int c = 0; c < 16; ++c) {
-        const uint4 w = p[c];
-        const float* kb = kbar + 8 * c;
-        d[0] = fma(bf16_lo(w.x), (double)kb[0], d[0]);
-        d[1] = fma(bf16_hi(w.x), (double)kb[1], d[1]);
-        d[2] = fma(bf16_lo(w.y), (double)kb[2], d[2]);
-        d[3] = fma(bf16_hi(w.y), (double)kb[3], d[3]);
-        d[0] = fma(bf16_lo(w.z), (double)kb[4], d[0]);
-        d[1] = fma(bf16_hi(w.z), (double)kb[5], d[1]);
-        d[2] = fma(bf16_lo(w.w), (double)kb[6], d[2]);
-        d[3] = fma(bf16_hi(w.w), (double)kb[7], d[3]);
-      }
-    } else if constexpr (QDT == FP_E4M3) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(q) + e0);
-#pragma unroll 2
-      for (int c = 0; c < 8; ++c) {
-        const uint4 w = p[c];
-        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
-        const float* kb = kbar + 16 * c;
+__device__ __forceinline__ void q_chunk8(const void* q, int64_t e0, int c, double* v) {
+  if constexpr (QDT == FP_BF16) {
+    const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(q) + e0)[c];
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  } else if constexpr (QDT == FP_E4M3) {
+    const uint2 w = reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(q) + e0)[c];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          d[e & 3] = fma((double)e4m3_to_f32((ws[e >> 2] >> (8 * (e & 3))) & 0xFFu), (double)kb[e], d[e & 3]);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e0);
-#pragma unroll 4
-      for (int c = 0; c < 32; ++c) {
-        const float4 v = p[c];
-        const float* kb = kbar + 4 * c;
-        d[0] = fma((double)(float)f32_to_bf16(v.x), (double)kb[0], d[0]);
-        d[1] = fma((double)(float)f32_to_bf16(v.y), (double)kb[1], d[1]);
-        d[2] = fma((double)(float)f32_to_bf16(v.z), (double)kb[2], d[2]);
-        d[3] = fma((double)(float)f32_to_bf16(v.w), (double)kb[3], d[3]);
-      }
-    }
-    double x = scale * ((d[0] + d[1]) + (d[2] + d[3]));
-    if constexpr (QDT == FP_E4M3) x *= (double)q_scale[hq_idx];
-    acc += exp(x - ref);
+    for (int e = 0; e < 8; ++e) v[e] = (double)e4m3_to_f32(((e < 4 ? w.x : w.y) >> (8 * (e & 3))) & 0xFFu);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e0) + 2 * c;
+    const float4 a = p[0], b = p[1];
+    const float t[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (double)(float)f32_to_bf16(t[e]);
   }
-  acc = wave_sum_d(acc);
-  return log(acc) + ref;
 }
 
-// The same exact score computed by a whole workgroup of kSelThreads threads
-// (rows split across all of them, one block-wide reduction).  Called
-// uniformly by every thread.
-constexpr int kSelThreads = 256;
-
+// Exact scores of nb <= kBatch pooled keys (fp32 kbar rows staged in LDS at
+// kbs[b * 128 ..]) for the rows of (h, block I), in one pass over the query
+// rows: ex[b] = ln sum_r exp(x_rb - ref) + ref, x_rb = scale * q_r . kbar_b,
+// all in float64.  Thread t takes rows t, t + 256, ...; each query row is read
+// once for all nb keys (two accumulators per key).  Called uniformly by every
+// thread; every thread returns the same ex[].
 template <int QDT>
-__device__ double exact_score_wg(const void* q, const float* q_scale, const float* kbar, int hq,
-                                 int group, int h, int64_t tok0, int nI, double scale, double ref,
-                                 double* red) {
+__device__ void exact_scores(const void* q, const float* q_scale, const float* kbs, int nb, int hq,
+                             int group, int h, int64_t tok0, int nI, double scale, double ref,
+                             double (*red)[kBatch], double* ex) {
   const int R = group * nI;
-  double acc = 0.0;
+  double acc[kBatch];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) acc[b] = 0.0;
   for (int r = threadIdx.x; r < R; r += kSelThreads) {
     const int hh = r / nI;
     const int t = r - hh * nI;
     const int hq_idx = h * group + hh;
     const int64_t e0 = ((tok0 + t) * hq + hq_idx) * (int64_t)kHeadDim;
-    double d[4] = {0.0, 0.0, 0.0, 0.0};
-    if constexpr (QDT == FP_BF16) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(q) + e0);
-#pragma unroll 4
-      for (int c = 0; c < 16; ++c) {
-        const uint4 w = p[c];
-        const float* kb = kbar + 8 * c;
-        d[0] = fma(bf16_lo(w.x), (double)kb[0], d[0]);
-        d[1] = fma(bf16_hi(w.x), (double)kb[1], d[1]);
-        d[2] = fma(bf16_lo(w.y), (double)kb[2], d[2]);
-        d[3] = fma(bf16_hi(w.y), (double)kb[3], d[3]);
-        d[0] = fma(bf16_lo(w.z), (double)kb[4], d[0]);
-        d[1] = fma(bf16_hi(w.z), (double)kb[5], d[1]);
-        d[2] = fma(bf16_lo(w.w), (double)kb[6], d[2]);
-        d[3] = fma(bf16_hi(w.w), (double)kb[7], d[3]);
-      }
-    } else if constexpr (QDT == FP_E4M3) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(q) + e0);
-#pragma unroll 2
-      for (int c = 0; c < 8; ++c) {
-        const uint4 w = p[c];
-        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
-        const float* kb = kbar + 16 * c;
+    double d0[kBatch], d1[kBatch];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          d[e & 3] = fma((double)e4m3_to_f32((ws[e >> 2] >> (8 * (e & 3))) & 0xFFu), (double)kb[e], d[e & 3]);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e0);
-#pragma unroll 4
-      for (int c = 0; c < 32; ++c) {
-        const float4 v = p[c];
-        const float* kb = kbar + 4 * c;
-        d[0] = fma((double)(float)f32_to_bf16(v.x), (double)kb[0], d[0]);
-        d[1] = fma((double)(float)f32_to_bf16(v.y), (double)kb[1], d[1]);
-        d[2] = fma((double)(float)f32_to_bf16(v.z), (double)kb[2], d[2]);
-        d[3] = fma((double)(float)f32_to_bf16(v.w), (double)kb[3], d[3]);
+    for (int b = 0; b < kBatch; ++b) d0[b] = d1[b] = 0.0;
+    // the staged keys are re-read every row (opaque offset), not kept live;
+    // the chunk loop stays rolled (unrolling it, or keeping several rows per
+    // thread in flight, measured slower: more registers, fewer waves)
+    int koff = 0;
+    asm volatile("" : "+v"(koff));
+#pragma unroll 1
+    for (int c = 0; c < kHeadDim / 8; ++c) {
+      double v[8];
+      q_chunk8<QDT>(q, e0, c, v);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (b < nb) {
+          const float4 k0 = *reinterpret_cast<const float4*>(kbs + koff + b * kHeadDim + 8 * c);
+          const float4 k1 = *reinterpret_cast<const float4*>(kbs + koff + b * kHeadDim + 8 * c + 4);
+          d0[b] = fma(v[0], (double)k0.x, d0[b]);
+          d1[b] = fma(v[1], (double)k0.y, d1[b]);
+          d0[b] = fma(v[2], (double)k0.z, d0[b]);
+          d1[b] = fma(v[3], (double)k0.w, d1[b]);
+          d0[b] = fma(v[4], (double)k1.x, d0[b]);
+          d1[b] = fma(v[5], (double)k1.y, d1[b]);
+          d0[b] = fma(v[6], (double)k1.z, d0[b]);
+          d1[b] = fma(v[7], (double)k1.w, d1[b]);
+        }
       }
     }
-    double x = scale * ((d[0] + d[1]) + (d[2] + d[3]));
-    if constexpr (QDT == FP_E4M3) x *= (double)q_scale[hq_idx];
-    acc += exp(x - ref);
-  }
-  acc = wave_sum_d(acc);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  double tot = 0.0;
+    const double sq = QDT == FP_E4M3 ? scale * (double)q_scale[hq_idx] : scale;
 #pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) tot += red[w];
-  __syncthreads();  // red is reused by the next call
-  return log(tot) + ref;
+    for (int b = 0; b < kBatch; ++b)
+      if (b < nb) acc[b] += exp(sq * (d0[b] + d1[b]) - ref);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    if (b < nb) {
+      const double v = wave_sum_d(acc[b]);
+      if (lane == 0) red[wave][b] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    if (b < nb) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kSelThreads / 64; ++w) tot += red[w][b];
+      ex[b] = log(tot) + ref;
+    }
+  }
+  __syncthreads();  // red and the staged keys are reused by the next batch
 }
 
 // One workgroup per CSR row.  Pass 1 (threads over J, wave ballots): the fast
-// keep bits and two candidate bitmaps in LDS, one for entries within kGuard of
-// the threshold (never forced blocks) and one for entries within kGuard of the
-// row max.  Pass 2, only if a threshold candidate exists: the exact row max
-// over the max candidates, then the exact decision of every threshold
-// candidate, each evaluated by the whole workgroup.  Pass 3 writes every word
-// of the row's bitmask and the count.
+// keep bits and two candidate bitmaps in LDS, one for entries within the guard
+// of the threshold (never forced blocks) and one for entries within the guard
+// of the row max.  Pass 2, only if a threshold candidate exists: the max
+// candidates and then the threshold candidates, in batches of kBatch keys
+// evaluated exactly in one pass over the row's queries each; the exact row
+// max is complete before the first threshold candidate is decided (the max
+// candidates come first).  Pass 3 writes every word of the row's bitmask and
+// the count.
 template <int QDT>
 __global__ __launch_bounds__(kSelThreads) void decide_kernel(
     SeqMap m, int hq, int kvdiv, int group, int64_t num_blocks, int64_t num_qblocks,
     int max_blocks, float softmax_scale,
     const void* __restrict__ q, const float* __restrict__ q_scale,
-    const float* __restrict__ k_mean, const float* __restrict__ scores, float alpha, int n_sink,
+    const float* __restrict__ k_mean, const float* __restrict__ scores,
+    const float* __restrict__ errb, float alpha, int n_sink,
     int n_local, uint32_t* __restrict__ keep_bits, int32_t* __restrict__ counts) {
   constexpr int kW = kMaxBlocksPerSeq / 32;
   __shared__ uint32_t keep_fast[kW + 1], cand_thr[kW + 1], cand_max[kW + 1], keep_fix[kW + 1];
   __shared__ float redf[kSelThreads / 64];
   __shared__ int redi[kSelThreads / 64];
-  __shared__ double redd[kSelThreads / 64];
+  __shared__ double redd[kSelThreads / 64][kBatch];
+  __shared__ __attribute__((aligned(16))) float kbs[kBatch * kHeadDim];
+  __shared__ int bj[kBatch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -217,6 +190,7 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   for (int w = 1; w < kSelThreads / 64; ++w) lmax = fmaxf(lmax, redf[w]);
   const float lna = __logf(alpha);
   const float thr = lna + lmax;
+  const float guard = kGuard + 2.f * errb[row];
 
   // pass 1: fast decisions and candidate bitmaps
   int need_l = 0;
@@ -227,8 +201,8 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
       const float l = L[J];
       const bool forced = J < n_sink || I - J < n_local;
       kp = forced || l >= thr;
-      ct = !forced && fabsf(l - thr) <= kGuard;
-      cm = l >= lmax - kGuard;
+      ct = !forced && fabsf(l - thr) <= guard;
+      cm = l >= lmax - guard;
     }
     const unsigned long long bk = __ballot(kp), bt = __ballot(ct), bm = __ballot(cm);
     need_l |= bt != 0ull;
@@ -256,31 +230,46 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
     // pooled keys of its KV head h / kvdiv
     const float* kb = k_mean + ((int64_t)(h / kvdiv) * num_blocks + qb.kb0) * kHeadDim;
     const double ref = (double)lmax;
+    const double lnalpha = log((double)alpha);
+    for (int w = tid; w < nw_row; w += kSelThreads) keep_fix[w] = 0u;
     double emax = -INFINITY;
-    for (int w = 0; w < nw_row; ++w) {
-      uint32_t m = cand_max[w];
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1u;
-        const double e = exact_score_wg<QDT>(q, q_scale, kb + (int64_t)(32 * w + b) * kHeadDim, hq,
-                                             group, h, tok0, nI, (double)softmax_scale, ref, redd);
-        emax = fmax(emax, e);
+    int nb = 0;
+    uint32_t thr_mask = 0u;  // batch entries that are threshold candidates
+    auto flush = [&]() {
+      __syncthreads();  // bj[] written by thread 0; keep_fix cleared
+      for (int e = tid; e < nb * kHeadDim; e += kSelThreads)
+        kbs[e] = kb[(int64_t)bj[e / kHeadDim] * kHeadDim + e % kHeadDim];
+      __syncthreads();
+      double ex[kBatch];
+      exact_scores<QDT>(q, q_scale, kbs, nb, hq, group, h, tok0, nI, (double)softmax_scale, ref,
+                        redd, ex);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (b < nb) {
+          if (!((thr_mask >> b) & 1u)) {
+            emax = fmax(emax, ex[b]);
+          } else if (tid == 0 && ex[b] >= lnalpha + emax) {
+            keep_fix[bj[b] >> 5] |= 1u << (bj[b] & 31);
+          }
+        }
+      }
+      __syncthreads();  // bj[] is rewritten by the next batch
+      nb = 0;
+      thr_mask = 0u;
+    };
+    for (int kind = 0; kind < 2; ++kind) {  // max candidates first, then threshold candidates
+      for (int w = 0; w < nw_row; ++w) {
+        uint32_t mw = kind == 0 ? cand_max[w] : cand_thr[w];
+        while (mw) {
+          const int b = __ffs(mw) - 1;
+          mw &= mw - 1u;
+          if (tid == 0) bj[nb] = 32 * w + b;
+          if (kind) thr_mask |= 1u << nb;
+          if (++nb == kBatch) flush();
+        }
       }
     }
-    const double ex_thr = log((double)alpha) + emax;
-    for (int w = 0; w < nw_row; ++w) {
-      uint32_t m = cand_thr[w];
-      uint32_t fix = 0u;
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1u;
-        const double e = exact_score_wg<QDT>(q, q_scale, kb + (int64_t)(32 * w + b) * kHeadDim, hq,
-                                             group, h, tok0, nI, (double)softmax_scale, ref, redd);
-        if (e >= ex_thr) fix |= 1u << b;
-      }
-      if (tid == 0) keep_fix[w] = fix;
-    }
-    __syncthreads();
+    if (nb) flush();
   }
 
   // pass 3: every word of the row (blocks past the diagonal are zero)
@@ -528,7 +517,8 @@ hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, cons
 #define FP_DEC(QD)                                                                              \
   hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, m, g.hq, g.kvdiv, \
                      g.lgroup, g.num_blocks, g.num_qblocks, g.max_blocks, g.softmax_scale, q,  \
-                     q_scale, k_mean, scores, alpha, n_sink, n_local, keep_bits, counts)
+                     q_scale, k_mean, scores, scores + g.num_rows * (int64_t)g.max_blocks, alpha, \
+                     n_sink, n_local, keep_bits, counts)
   if (g.qk_dtype == FP_BF16) FP_DEC(FP_BF16);
   else if (g.qk_dtype == FP_E4M3) FP_DEC(FP_E4M3);
   else if (g.qk_dtype == FP_F32) FP_DEC(FP_F32);

@@ -83,8 +83,12 @@ class Pipeline:
         f32 = torch.float32
         self.k_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
         self.v_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
-        # score rows per index-list owner (KV head, or query head with head_lists)
-        self.scores = torch.empty((p.list_owners, NQ, p.max_blocks), dtype=f32, device=dev)
+        # score rows per index-list owner (KV head, or query head with head_lists),
+        # then one error bound per score row (scores_err)
+        nsc = p.list_owners * NQ * p.max_blocks
+        self.scores_buf = torch.empty(p.scores_elems, dtype=f32, device=dev)
+        self.scores = self.scores_buf[:nsc].view(p.list_owners, NQ, p.max_blocks)
+        self.scores_err = self.scores_buf[nsc:].view(p.list_owners, NQ)
         self.row_ptr = torch.empty(p.num_rows + 1, dtype=torch.int32, device=dev)
         self.col_idx = torch.empty(p.csr_capacity, dtype=torch.int32, device=dev)
         odt = torch.float32 if db.out_dtype == "f32" else torch.bfloat16

@@ -139,7 +139,9 @@ int64_t fp_num_blocks(const fp_problem* p);       /* N = sum_s nk_s (pooled rows
 int64_t fp_num_query_blocks(const fp_problem* p); /* NQ = sum_s nq_s              */
 int32_t fp_max_blocks(const fp_problem* p);       /* n_max                        */
 int64_t fp_num_rows(const fp_problem* p);         /* Lo * NQ (CSR rows)           */
-int64_t fp_scores_elems(const fp_problem* p);     /* Lo * NQ * n_max              */
+int64_t fp_scores_elems(const fp_problem* p);     /* Lo * NQ * (n_max + 1): the
+                                                     scores, then one error bound
+                                                     per score row               */
 int64_t fp_csr_capacity(const fp_problem* p);     /* Lo * sum over query blocks of
                                                      (I + 1): every causal block kept */
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which);
@@ -166,10 +168,13 @@ const char* fp_last_error(void);
  * block is a subtraction of max_J of this value (done by fp_select).
  * Entries with J > I are left unspecified.
  *
- * The dot products run on bf16 MFMA with kbar split into two bf16 terms
- * (hi + lo, fp32 accumulation); the result carries an absolute error of a
- * few 1e-5 (natural-log units) on attention-scale logits, which fp_select
- * accounts for.
+ * The dot products run on bf16 MFMA with kbar rounded to bf16 (fp32
+ * accumulation).  After the Lo * NQ * n_max scores, block_scores holds one
+ * float per score row (same row order): a bound E on |fast - exact| for
+ * every entry of the row, E = softmax_scale * max_r |q_r|_2 *
+ * max_{J<=I} (|kbar_J - bf16(kbar_J)|_2 + 2^-17 |bf16(kbar_J)|_2)
+ * (Cauchy-Schwarz on the rounding of kbar, plus the fp32 accumulation of 128
+ * exact products; |q_r| includes q_scale for e4m3), which fp_select uses.
  *
  * q, k_cache, v_cache: inputs (layouts above).  k_mean, v_mean, block_scores:
  * outputs.  ws: FP_WS_DISCOVER workspace.
@@ -191,10 +196,11 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache,
  * Kept indices are written ascending (compaction, same summary 3.3).
  *
  * Because block_scores comes from a bf16 fast path, every entry whose fast
- * value lies within 2e-3 (natural-log units) of the threshold, together
- * with the row's candidates for the maximum, is re-evaluated from q and
- * k_mean in float64 before it is decided; all other decisions have a margin
- * far larger than the fast path's error.
+ * value lies within 2 E + 2e-3 (natural-log units; E = the row's bound
+ * stored after the scores, 2e-3 an allowance for the fp32 statistics) of the
+ * threshold, together with the row's candidates for the maximum, is
+ * re-evaluated from q and k_mean in float64 before it is decided; every
+ * other decision is the same as in exact arithmetic.
  *
  * q, k_mean, block_scores: inputs from the same problem.  row_ptr
  * [fp_num_rows + 1], col_idx [col_capacity]: outputs.  col_capacity must be

@@ -59,7 +59,7 @@ def test_size_queries(bind):
     assert p.num_blocks == sum(n)
     assert p.max_blocks == 8
     assert p.num_rows == 2 * sum(n)
-    assert p.scores_elems == 2 * sum(n) * 8
+    assert p.scores_elems == 2 * sum(n) * (8 + 1)  # scores + one bound per row
     assert p.csr_capacity == 2 * sum(x * (x + 1) // 2 for x in n)
     for which in (bind.FP_WS_DISCOVER, bind.FP_WS_SELECT, bind.FP_WS_ATTN):
         assert p.workspace_bytes(which) > 0
@@ -111,7 +111,7 @@ def test_size_queries_chunked_prefill(bind):
     assert p.num_query_blocks == sum(nq)
     assert p.max_blocks == 9
     assert p.num_rows == 2 * sum(nq)
-    assert p.scores_elems == 2 * sum(nq) * 9
+    assert p.scores_elems == 2 * sum(nq) * (9 + 1)
     assert p.csr_capacity == 2 * sum(a * (a + 1) // 2 - b * (b + 1) // 2 for a, b in zip(nk, i0))
 
 
@@ -148,7 +148,7 @@ def test_size_queries_per_query_head_lists(bind):
     assert per.list_owners == 8 and base.list_owners == 2
     assert per.num_blocks == base.num_blocks == sum(n)
     assert per.num_rows == 8 * sum(n)
-    assert per.scores_elems == 8 * sum(n) * 8
+    assert per.scores_elems == 8 * sum(n) * (8 + 1)
     assert per.csr_capacity == 4 * base.csr_capacity
     assert per.workspace_bytes(bind.FP_WS_SELECT) > base.workspace_bytes(bind.FP_WS_SELECT)
     bad = _problem(bind)

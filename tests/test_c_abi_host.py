@@ -49,7 +49,7 @@ def test_c_program_uses_the_abi(tmp_path):
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines()
     n = [3, 2, 1, 8]                       # key blocks per sequence
     causal = sum(x * (x + 1) // 2 for x in n)
-    assert out[0].split() == [str(v) for v in (sum(n), sum(n), 8, 2 * sum(n), 2 * sum(n) * 8,
+    assert out[0].split() == [str(v) for v in (sum(n), sum(n), 8, 2 * sum(n), 2 * sum(n) * (8 + 1),
                                                  2 * causal)]
     assert out[1].split() == [str(8 * sum(n)), str(8 * causal)]
     rows, msg, status = out[2].split("|")
