@@ -1,0 +1,63 @@
+"""GPU parity where the fast scores' error bound is wide: queries scaled up so
+that the selection's float64 band holds many entries per row (more than one
+batch of re-checked keys, max candidates included), compared in full with
+the oracle."""
+
+import numpy as np
+import pytest
+
+from oracle import OracleProblem, pool_blocks, run_pipeline
+from oracle.flashprefill import decode_bf16
+from synthetic import custom_spec, make_workload
+from synthetic.workloads import encode_bf16
+
+from gpu_parity_util import compare, log, run_gpu, score_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def wide_band_workload(c):
+    """Every query of KV group h gets c * u_h added, u_h a unit vector
+    orthogonal to all pooled keys of KV head h (fewer blocks than dimensions):
+    the pooled logits barely move, the query norms, and with them the fast
+    scores' error bound, grow with c."""
+    w = make_workload(custom_spec((3000, 1100), 8, 2, page_size=32, seed=4242, name="wideband"))
+    prob = OracleProblem.from_workload(w)
+    q = decode_bf16(w.q).astype(np.float64)
+    g = prob.group
+    for h in range(prob.hkv):
+        kb = np.concatenate([pool_blocks(prob.keys(s, h), prob.block_size)[0]
+                             for s in range(prob.num_seqs)])
+        u = np.linalg.svd(kb)[2][-1]  # right singular vector of a zero singular value
+        assert np.max(np.abs(kb @ u)) < 1e-9
+        q[:, h * g:(h + 1) * g, :] += c * u
+    w.q = encode_bf16(q.astype(np.float32))
+    return w
+
+
+@pytest.mark.parametrize("alpha", [0.1, 0.02])
+def test_wide_error_band_parity(alpha):
+    w = wide_band_workload(200.0)
+    prob = OracleProblem.from_workload(w)
+    # how many entries the library has to re-check (computed from the
+    # oracle's scores and the bound recomputed from its inputs)
+    res = run_pipeline(prob, alpha, attend=False)
+    pooled = np.zeros((prob.hkv, int(prob.block_offsets()[-1]), prob.d), dtype=np.float32)
+    for s in range(prob.num_seqs):
+        for h in range(prob.hkv):
+            km, _ = pool_blocks(prob.keys(s, h), prob.block_size)
+            b0 = int(prob.block_offsets()[s])
+            pooled[h, b0:b0 + len(km)] = km
+    most = 0
+    total = 0
+    for (h, s, I), r in res.items():
+        g = 2 * score_bound(prob, pooled, h, s, I) + 2e-3
+        L = r["L"]
+        n = int(np.sum(np.abs(L - (L.max() + np.log(alpha))) <= g)) + int(np.sum(L >= L.max() - g))
+        most = max(most, n)
+        total += n
+    log(f"  wide band alpha={alpha}: up to {most} re-checked keys per row, {total} in all")
+    assert most > 8  # several batches of re-checked keys in one row
+    g = run_gpu(w, alpha)
+    stats = compare(w, g, alpha)
+    assert stats["score_bound"] > 0.2
