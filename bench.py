@@ -246,6 +246,83 @@ def cpu_baseline(w, alpha, correction, budget_s=20.0, seed=0):
     }
 
 
+def oracle_scores(w, threads=16):
+    """Part of the oracle (cpu_baseline) leg: the fp64 oracle's block scores
+    of every (list owner, sequence, query block) row of the workload, list
+    owners in parallel threads.  They do not depend on alpha."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import OracleProblem, run_pipeline
+    prob = OracleProblem.from_workload(w)
+
+    def owner(h):
+        rows = [(h, s, I) for s in range(prob.num_seqs) for I in prob.query_blocks(s)]
+        return {k: r["L"] for k, r in run_pipeline(prob, 1.0, rows=rows, attend=False).items()}
+
+    scores = {}
+    with ThreadPoolExecutor(min(threads, prob.list_owners)) as ex:
+        for part in ex.map(owner, range(prob.list_owners)):
+            scores.update(part)
+    return prob, scores
+
+
+def oracle_parity(w, prob, scores, pipe, alpha, correction, rows_per_head=2, seed=0):
+    """Part of the oracle (cpu_baseline) leg: the GPU step's results against
+    the fp64 oracle on the host.  Index lists: every row against the
+    oracle's selection from its float64 scores (entries inside the oracle's
+    1e-5 band at the threshold are counted, not compared).  Outputs and lse:
+    a seeded sample of rows per list owner (first and last block included)
+    against the oracle fed the GPU's own lists.  Returns the fields of the
+    measurement line's `parity` object."""
+    import torch
+    from oracle import run_pipeline, select_row
+    t0 = time.time()
+    torch.cuda.synchronize()
+    rp, ci = pipe.csr()
+    out = pipe.out.float().cpu().numpy()
+    lse = pipe.lse.cpu().numpy()
+    B = prob.block_size
+    band = mism = 0
+    for (h, s, I), L in scores.items():
+        kept, flag = select_row(L, I, alpha, 256, 512, B)
+        row = prob.row_index(h, s, I)
+        fl = set(np.nonzero(flag)[0].tolist())
+        band += len(fl)
+        mism += len((set(ci[rp[row]:rp[row + 1]].tolist()) ^ set(kept.tolist())) - fl)
+    rng = np.random.default_rng(seed)
+    sample = []
+    for s in range(prob.num_seqs):
+        qb = list(prob.query_blocks(s))
+        for h in range(prob.list_owners):
+            pick = {qb[0], qb[-1]} | set(int(x) for x in rng.choice(qb, min(len(qb), rows_per_head),
+                                                                     replace=False))
+            sample += [(h, s, I) for I in sorted(pick)]
+    res = run_pipeline(prob, alpha, correction=correction, rows=sample, given_csr=(rp, ci))
+    emax = esum = lmax = 0.0
+    n = 0
+    for (h, s, I), r in res.items():
+        heads = prob.list_heads(h)
+        toks = int(w.cu_seqlens[s]) + I * B - prob.ctx(s) + np.arange(r["out"].shape[1])
+        d = np.abs(out[toks][:, heads, :].transpose(1, 0, 2) - r["out"])
+        emax = max(emax, float(d.max()))
+        esum += float(d.sum())
+        n += d.size
+        lmax = max(lmax, float(np.abs(lse[heads][:, toks] - r["lse"]).max()))
+    return {
+        "rows": len(scores),
+        "in_band": int(band),
+        "mismatches": int(mism),
+        "max_abs_err": round(emax, 6),
+        "mean_abs_err": float("%.3g" % (esum / max(1, n))),
+        "lse_max_abs_err": round(lmax, 6),
+        "sampled_rows": len(res),
+        "tolerance": {"bf16": 2e-2, "f32": 2e-2, "e4m3": 6e-2}[w.spec.qk_dtype],
+        "oracle": "fp64 CPU oracle: lists of every row; outputs and lse of the sampled rows, "
+                  "fed the GPU's lists",
+        "seconds": round(time.time() - t0, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +440,16 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # the oracle (cpu_baseline) leg: first the correctness of the timed step
+    # (before any other configuration overwrites its results), at the end the
+    # oracle's own throughput on a bounded sample
+    oracle_leg = not args.no_cpu_baseline and ctx is None and select is None and not hl
+    oscores = None
+    if oracle_leg:
+        t_or = time.time()
+        oprob, oscores = oracle_scores(w)
+        line["parity"] = oracle_parity(w, oprob, oscores, pipe, args.alpha, correction)
+        line["parity"]["oracle_scores_s"] = round(time.time() - t_or, 1)
     if args.attn_splits:
         line["config"]["attn_splits"] = args.attn_splits
     if select is not None:
@@ -391,9 +478,14 @@ def main():
                                block_density=int(r2[-1]) / cblocks,
                                pair_density=k2 / causal,
                                eff_tflops=4 * d * k2 / (ts["step_ms"] * 1e-3) / 1e12, **ts)
+                    if oscores is not None:
+                        pf = oracle_parity(w, oprob, oscores, pipe, a, corr)
+                        rec.update(in_band=pf["in_band"], mismatches=pf["mismatches"],
+                                   max_abs_err=pf["max_abs_err"], mean_abs_err=pf["mean_abs_err"],
+                                   lse_max_abs_err=pf["lse_max_abs_err"])
                     f.write(json.dumps(rec) + "\n")
                     print("# sweep " + json.dumps(rec), file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline and ctx is None and select is None and not hl:
+    if oracle_leg:
         line["cpu_baseline"] = cpu_baseline(w, args.alpha, correction, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)
 

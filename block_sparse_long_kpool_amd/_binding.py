@@ -114,6 +114,16 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _ptr_f64(t) -> Optional[int]:
+    """Pointer of a float64 tensor (the pooled means are float64 in the ABI)."""
+    if t is None:
+        return None
+    import torch
+    if isinstance(t, torch.Tensor) and t.dtype != torch.float64:
+        raise TypeError(f"pooled means must be float64 tensors, got {t.dtype}")
+    return _ptr(t)
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -218,14 +228,14 @@ class Problem:
 
 def fp_discover(p: Problem, q, k_cache, v_cache, k_mean, v_mean, block_scores, ws,
                 stream=None) -> None:
-    _check(p.lib.fp_discover(p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_mean),
-                             _ptr(v_mean), _ptr(block_scores), _ptr(ws), ws.numel() * ws.element_size(),
+    _check(p.lib.fp_discover(p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr_f64(k_mean),
+                             _ptr_f64(v_mean), _ptr(block_scores), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(stream)))
 
 
 def fp_select(p: Problem, q, k_mean, block_scores, alpha: float, sink_tokens: int,
               local_tokens: int, row_ptr, col_idx, ws, stream=None) -> None:
-    _check(p.lib.fp_select(p.ref, _ptr(q), _ptr(k_mean), _ptr(block_scores), float(alpha),
+    _check(p.lib.fp_select(p.ref, _ptr(q), _ptr_f64(k_mean), _ptr(block_scores), float(alpha),
                            int(sink_tokens), int(local_tokens), _ptr(row_ptr), _ptr(col_idx),
                            col_idx.numel(), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)))
@@ -249,5 +259,5 @@ def fp_sparse_attn_paged(p: Problem, q, k_cache, v_cache, row_ptr, col_idx, k_me
                          mean_correction: bool, out, lse, ws, stream=None) -> None:
     _check(p.lib.fp_sparse_attn_paged(
         p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(row_ptr), _ptr(col_idx),
-        _ptr(k_mean), _ptr(v_mean), 1 if mean_correction else 0, _ptr(out), _ptr(lse), _ptr(ws),
+        _ptr_f64(k_mean), _ptr_f64(v_mean), 1 if mean_correction else 0, _ptr(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,6 +1,7 @@
 // C ABI of the library: argument validation, size queries, workspace layout
 // and kernel launches.  Nothing here allocates device memory or synchronises.
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -54,7 +55,7 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   if (cu[0] != 0) return fail(FP_ERR_INVALID, "cu_seqlens[0] must be 0");
   if ((p->ctx_lens_host == nullptr) != (p->ctx_lens_dev == nullptr))
     return fail(FP_ERR_INVALID, "ctx_lens_host and ctx_lens_dev must both be set or both be NULL");
-  int64_t nblk = 0, nqblk = 0;
+  int64_t nblk = 0, nqblk = 0, causal = 0;
   int maxn = 0, maxlen = 0;
   for (int s = 0; s < p->num_seqs; ++s) {
     const int qlen = cu[s + 1] - cu[s];
@@ -69,6 +70,8 @@ int make_geometry(const fp_problem* p, Geometry* g) {
     const int n = (len + kBlock - 1) / kBlock;
     nblk += n;
     nqblk += n - c / kBlock;
+    const int64_t i0 = c / kBlock;  // first query block
+    causal += (int64_t)n * (n + 1) / 2 - i0 * (i0 + 1) / 2;
     maxn = std::max(maxn, n);
     maxlen = std::max(maxlen, len);
   }
@@ -93,11 +96,18 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   g->lgroup = p->head_lists ? 1 : p->num_q_heads / p->num_kv_heads;
   g->kvdiv = p->head_lists ? p->num_q_heads / p->num_kv_heads : 1;
   g->num_rows = nqblk * g->lists;
+  // row_ptr and col_idx offsets are int32: the list of every causal block
+  // (the capacity col_idx must have) has to fit
+  g->csr_capacity = causal * g->lists;
+  if (g->csr_capacity > (int64_t)INT32_MAX)
+    return fail(FP_ERR_UNSUPPORTED, "index lists of %lld entries (every causal block) exceed the "
+                "int32 offsets of row_ptr", (long long)g->csr_capacity);
   g->total_tokens = cu[p->num_seqs];
   g->qk_dtype = qk;
   g->v_dtype = vd;
   g->out_dtype = od;
   g->softmax_scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  g->softmax_scale_d = p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / sqrt((double)kHeadDim);
   if (p->attn_splits < 0) return fail(FP_ERR_INVALID, "attn_splits must be >= 0 (got %d)", p->attn_splits);
   g->attn_splits = p->attn_splits;
   return FP_OK;
@@ -209,15 +219,7 @@ int64_t fp_scores_elems(const fp_problem* p) {
 
 int64_t fp_csr_capacity(const fp_problem* p) {
   Geometry g;
-  if (make_geometry(p, &g) != FP_OK) return -1;
-  int64_t c = 0;
-  for (int s = 0; s < p->num_seqs; ++s) {
-    const int64_t ctx = p->ctx_lens_host ? p->ctx_lens_host[s] : 0;
-    const int64_t n = (ctx + p->cu_seqlens_host[s + 1] - p->cu_seqlens_host[s] + kBlock - 1) / kBlock;
-    const int64_t i0 = ctx / kBlock;  // first query block
-    c += n * (n + 1) / 2 - i0 * (i0 + 1) / 2;
-  }
-  return c * g.lists;
+  return make_geometry(p, &g) == FP_OK ? g.csr_capacity : -1;
 }
 
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which) {
@@ -241,7 +243,7 @@ const char* fp_status_string(int32_t status) {
 const char* fp_last_error(void) { return g_err; }
 
 int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const void* v_cache,
-                float* k_mean, float* v_mean, float* block_scores, void* ws, size_t ws_bytes,
+                double* k_mean, double* v_mean, float* block_scores, void* ws, size_t ws_bytes,
                 void* stream) {
   Geometry g;
   int st = make_geometry(p, &g);
@@ -261,7 +263,7 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const v
                     "scores");
 }
 
-int fp_select(const fp_problem* p, const void* q, const float* k_mean, const float* block_scores,
+int fp_select(const fp_problem* p, const void* q, const double* k_mean, const float* block_scores,
               float alpha, int32_t sink_tokens, int32_t local_tokens, int32_t* row_ptr,
               int32_t* col_idx, int64_t col_capacity, void* ws, size_t ws_bytes, void* stream) {
   Geometry g;
@@ -272,7 +274,7 @@ int fp_select(const fp_problem* p, const void* q, const float* k_mean, const flo
   if (sink_tokens < 0 || local_tokens < 0)
     return fail(FP_ERR_INVALID, "sink_tokens and local_tokens must be >= 0");
   if (isnan(alpha)) return fail(FP_ERR_INVALID, "alpha is NaN");
-  const int64_t cap = fp_csr_capacity(p);
+  const int64_t cap = g.csr_capacity;
   if (col_capacity < cap)
     return fail(FP_ERR_CAPACITY, "col_capacity %lld < %lld (every causal block kept)",
                 (long long)col_capacity, (long long)cap);
@@ -301,7 +303,7 @@ int select_ranked(const fp_problem* p, const float* block_scores, int mode, int3
     return fail(FP_ERR_INVALID, "sink_tokens and local_tokens must be >= 0");
   if (mode == 0 && top_k < 0) return fail(FP_ERR_INVALID, "top_k must be >= 0 (got %d)", top_k);
   if (mode == 1 && !(top_p == top_p)) return fail(FP_ERR_INVALID, "top_p is NaN");
-  const int64_t cap = fp_csr_capacity(p);
+  const int64_t cap = g.csr_capacity;
   if (col_capacity < cap)
     return fail(FP_ERR_CAPACITY, "col_capacity %lld < %lld (every causal block kept)",
                 (long long)col_capacity, (long long)cap);
@@ -334,8 +336,8 @@ int fp_select_topp(const fp_problem* p, const float* block_scores, float top_p, 
 }
 
 int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* row_ptr, const int32_t* col_idx, const float* k_mean,
-                         const float* v_mean, int32_t mean_correction, void* out, float* lse, void* ws,
+                         const int32_t* row_ptr, const int32_t* col_idx, const double* k_mean,
+                         const double* v_mean, int32_t mean_correction, void* out, float* lse, void* ws,
                          size_t ws_bytes, void* stream) {
   Geometry g;
   int st = make_geometry(p, &g);

@@ -10,8 +10,8 @@
 //
 // gfx950 design:
 //   * workgroup = 256 query rows = 2 heads of one GQA group x the 128 tokens
-//     of one query block, split over kAttnWaves waves (8: two waves per SIMD,
-//     one 32-row chunk each; 4: one wave per SIMD, two chunks each).  The g/2
+//     of one query block, split over 8 waves (two per SIMD, one 32-row chunk
+//     each).  The g/2
 //     workgroups of a group get consecutive ids on the same XCD so their K/V
 //     reads share that L2.
 //   * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no staging
@@ -61,11 +61,9 @@ constexpr float kLazyBound = 18446744073709551616.0f;  // 2^kLazy
 // correction tile, whose first chunk can be fully masked for some rows.)
 constexpr float kMInit = -1e30f;
 constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
-#ifndef FP_ATTN_WAVES
-#define FP_ATTN_WAVES 8
-#endif
-// waves per workgroup: 8 = two waves per SIMD, 32 query rows each
-constexpr int kAttnWaves = FP_ATTN_WAVES;
+// waves per workgroup: two waves per SIMD, 32 query rows each (a form with
+// four waves of 64 rows needs more than 512 registers per wave and spills)
+constexpr int kAttnWaves = 8;
 
 struct AttnArgs {
   SeqMap m;
@@ -127,6 +125,7 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
 
 template <int QDT, int VDT, int ODT, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
+  static_assert(NW == kAttnWaves, "one 32-row chunk per wave");
   constexpr int RC = 8 / NW;   // 32-row chunks per wave (the workgroup always covers 256 rows)
   constexpr int NT = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -805,9 +804,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 }
 
 // Block offsets of the map (last block of the grid) and bf16 copies of the
-// pooled keys / values.
-__global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const float* __restrict__ km,
-                                                        const float* __restrict__ vm, u16* __restrict__ km16,
+// pooled keys / values (each rounded once from float64).
+__global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const double* __restrict__ km,
+                                                        const double* __restrict__ vm, u16* __restrict__ km16,
                                                         u16* __restrict__ vm16, int64_t n) {
   if (blockIdx.x == gridDim.x - 1) {
     plan_offsets(m);
@@ -816,16 +815,21 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const float* _
   if (km == nullptr) return;
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
-  const float4 x = *reinterpret_cast<const float4*>(km + i);
-  const float4 y = *reinterpret_cast<const float4*>(vm + i);
-  *reinterpret_cast<uint2*>(km16 + i) = f32x4_to_bf16x4(x);
-  *reinterpret_cast<uint2*>(vm16 + i) = f32x4_to_bf16x4(y);
+  const double2* kp = reinterpret_cast<const double2*>(km + i);
+  const double2* vp = reinterpret_cast<const double2*>(vm + i);
+  const double2 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+  const ushort4 kb = make_ushort4(f64_to_bf16_bits(k0.x), f64_to_bf16_bits(k0.y),
+                                  f64_to_bf16_bits(k1.x), f64_to_bf16_bits(k1.y));
+  const ushort4 vb = make_ushort4(f64_to_bf16_bits(v0.x), f64_to_bf16_bits(v0.y),
+                                  f64_to_bf16_bits(v1.x), f64_to_bf16_bits(v1.y));
+  *reinterpret_cast<ushort4*>(km16 + i) = kb;
+  *reinterpret_cast<ushort4*>(vm16 + i) = vb;
 }
 
 }  // namespace
 
-hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_mean,
-                            const float* v_mean, u16* km16, u16* vm16, hipStream_t st) {
+hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const double* k_mean,
+                            const double* v_mean, u16* km16, u16* vm16, hipStream_t st) {
   const int64_t n = (int64_t)g.hkv * g.num_blocks * kHeadDim;
   const unsigned conv = k_mean ? (unsigned)((n / 4 + 255) / 256) : 0u;
   hipLaunchKernelGGL(attn_prep_kernel, dim3(conv + 1), dim3(256), 0, st, m, k_mean, v_mean, km16,
@@ -881,13 +885,9 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   const size_t shm = sizeof(SharedMem);
 #define FP_ATTN(QD, VD, OD)                                                                    \
   do {                                                                                         \
-    static bool attr_set = false;                                                              \
-    if (!attr_set) {                                                                           \
-      hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<QD, VD, OD, kAttnWaves>,     \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm); \
-      if (e != hipSuccess) return e;                                                           \
-      attr_set = true;                                                                         \
-    }                                                                                          \
+    static std::atomic<uint64_t> smem_set;                                                     \
+    const hipError_t ea = set_smem_limit(smem_set, (const void*)attn_kernel<QD, VD, OD, kAttnWaves>, shm); \
+    if (ea != hipSuccess) return ea;                                                           \
     hipLaunchKernelGGL((attn_kernel<QD, VD, OD, kAttnWaves>), dim3(grid), dim3(64 * kAttnWaves), shm, st, a); \
   } while (0)
 #define FP_ATTN_O(QD, VD)                                  \

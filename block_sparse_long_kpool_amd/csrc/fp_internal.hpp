@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/flashprefill.h"
 
 namespace fp {
@@ -32,13 +34,16 @@ struct Geometry {
   int64_t num_qblocks;   // NQ = sum_s nq_s query blocks (score / CSR rows per KV head)
   int max_blocks;        // max_s nk_s
   int64_t num_rows;      // lists * NQ (score / CSR rows)
+  int64_t csr_capacity;  // lists * causal blocks of the query blocks (<= INT32_MAX)
   // Index-list owners: the KV heads (lists = Hkv, lgroup = group query heads
   // per list, kvdiv = 1) or, per query head, lists = Hq, lgroup = 1 and
   // kvdiv = group (owner o reads KV head o / kvdiv).
   int lists, lgroup, kvdiv;
   int64_t total_tokens;  // T (query tokens)
   int qk_dtype, v_dtype, out_dtype;
-  float softmax_scale;
+  float softmax_scale;     // fp32 logit scale of the fast paths
+  double softmax_scale_d;  // the same scale in float64 (1/sqrt(128) unrounded by
+                           // default) for the exact re-evaluation
   int attn_splits;  // requested KV split of the attention (0: automatic)
 };
 
@@ -80,6 +85,24 @@ __device__ __forceinline__ float e4m3_to_f32(unsigned c) {
 }
 
 __device__ __forceinline__ __bf16 f32_to_bf16(float x) { return (__bf16)x; }
+
+// float64 -> bf16 bits, rounded once to nearest even: truncate to fp32, set
+// the fp32 sticky bit when that was inexact (round to odd), then round the
+// fp32 value to nearest even (24 >= 8 + 2 bits, so the two steps equal one
+// correct rounding).  Finite inputs.
+__device__ __forceinline__ u16 f64_to_bf16_bits(double x) {
+  const float t = __double2float_rz(x);
+  const unsigned odd = (double)t != x ? 1u : 0u;
+  const float f = __uint_as_float(__float_as_uint(t) | odd);
+  return __builtin_bit_cast(u16, f32_to_bf16(f));
+}
+
+// Relative error allowance of a 128-term fp32 dot product of exactly
+// representable products (MFMA with fp32 accumulation): n - 1 additions,
+// each off by less than one ulp (2^-23, which covers truncating as well as
+// nearest rounding), give less than 127 * 2^-23 < 2^-16 of the sum of the
+// absolute products; kAccumRel doubles that.
+constexpr double kAccumRel = 0x1p-15;
 
 // Locate global block gb: sequence s with boff[s] <= gb < boff[s+1].
 __device__ __forceinline__ int find_seq(const int* __restrict__ boff, int num_seqs, int gb) {
@@ -241,16 +264,31 @@ __device__ __forceinline__ void interleave() {
 
 // ---- launchers (one per translation unit) ---------------------------------
 
+// Raise a kernel's dynamic LDS limit to `bytes` once per device (bit d of
+// `done` records device d; devices >= 64 are set on every launch).  Racing
+// host threads may both set it, which is harmless: the call is idempotent.
+inline hipError_t set_smem_limit(std::atomic<uint64_t>& done, const void* fn, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 // Block offsets kboff / qboff of the map (one workgroup).
 hipError_t launch_plan(const SeqMap& m, hipStream_t st);
 
-// Pooling also writes kbar rounded to bf16 and, per key block, the bound
-// kres_J = |kbar_J - bf16(kbar_J)|_2 + 2^-17 |bf16(kbar_J)|_2 on how far a
-// query row of unit norm can move its bf16 dot product with kbar_J (rounding
-// of kbar, plus fp32 accumulation of 128 exact products).
+// Pooling (float64 means) also writes kbar rounded to bf16 and, per key
+// block, the bound kres_J = |kbar_J - bf16(kbar_J)|_2 + kAccumRel
+// |bf16(kbar_J)|_2 on how far a query row of unit norm can move its bf16 dot
+// product with kbar_J from the exact one (rounding of kbar, plus fp32
+// accumulation of 128 exact products).
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
-                       float* k_mean, float* v_mean, u16* k_mean_bf16, float* kres,
+                       double* k_mean, double* v_mean, u16* k_mean_bf16, float* kres,
                        hipStream_t st);
 
 // Scores [lists * NQ, max_blocks] followed by one error bound per score row.
@@ -259,7 +297,7 @@ hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, cons
                          hipStream_t st);
 
 hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
-                         const float* k_mean, const float* scores, float alpha, int n_sink,
+                         const double* k_mean, const float* scores, float alpha, int n_sink,
                          int n_local, uint32_t* keep_bits, int32_t* counts, int32_t* row_ptr,
                          int32_t* col_idx, hipStream_t st);
 
@@ -270,8 +308,8 @@ hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float*
                                 int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);
 
 // Block offsets of the map plus bf16 copies of the pooled keys / values.
-hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const float* k_mean,
-                            const float* v_mean, u16* km16, u16* vm16, hipStream_t st);
+hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const double* k_mean,
+                            const double* v_mean, u16* km16, u16* vm16, hipStream_t st);
 
 // Parts per row of the attention launch (1: no split).
 int attn_splits(const Geometry& g);

@@ -1,7 +1,7 @@
 // Block pooling: mean of K and V over each 128-token block of the paged
 // cache (FlashPrefill summary "长上下文加速 28 倍", 3.1 key pooling; FlashPrefill
-// V2 paper reading 4.1, the block means kbar_J / vbar_J).  HBM-bound: every
-// K/V element is read exactly once.
+// V2 paper reading 4.1, the block means kbar_J / vbar_J), in float64.
+// HBM-bound: every K/V element is read exactly once.
 #include "fp_internal.hpp"
 
 namespace fp {
@@ -42,15 +42,19 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) 
 
 // grid (NK key blocks, Hkv, 2 = {K, V}); 256 threads = 16 token lanes x 16
 // chunks of 8 head-dim elements.  Every key block of the cache is pooled,
-// cached prefix included.  Summation order is fixed (deterministic).
+// cached prefix included.  The sums run in float64: the at most 128 stored
+// values of a block (bf16 or e4m3 codes, 8 and 4 significant bits) add up
+// exactly unless their magnitudes span more than ~2^38, and the division by
+// n_J rounds once, so the means are the exact block means to float64
+// rounding.  Summation order is fixed (deterministic).
 template <int KDT, int VDT>
 __global__ __launch_bounds__(256) void pool_kernel(
     SeqMap m, const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
     int64_t num_blocks, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
-    const float* __restrict__ k_scale, float* __restrict__ k_mean, float* __restrict__ v_mean,
+    const float* __restrict__ k_scale, double* __restrict__ k_mean, double* __restrict__ v_mean,
     u16* __restrict__ k_mean_bf16, float* __restrict__ kres) {
-  __shared__ float red[16][kHeadDim + 4];
-  __shared__ float2 nred[kHeadDim / 64];
+  __shared__ double red[16][kHeadDim + 2];
+  __shared__ double2 nred[kHeadDim / 64];
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z == 1;
@@ -61,9 +65,9 @@ __global__ __launch_bounds__(256) void pool_kernel(
   const int nJ = min(kBlock, len - p0);
   const int chunk = threadIdx.x & 15;
   const int tl = threadIdx.x >> 4;
-  float acc[8];
+  double acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
   const int32_t* prow = page_table + (int64_t)s * max_pages;
   auto row_elem = [&](int p, int page) {
     return (((int64_t)page * page_size + p % page_size) * hkv + h) * kHeadDim + chunk * 8;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
 #pragma unroll
     for (int it = 0; it < kBlock / 16; ++it)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[it][i];
+      for (int i = 0; i < 8; ++i) acc[i] += (double)v[it][i];
   } else {
     for (int t = tl; t < nJ; t += 16) {
       const int p = p0 + t;
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
       const int64_t elem = row_elem(p, prow[p / page_size]);
       if (is_v) load8<VDT>(v_cache, elem, v); else load8<KDT>(k_cache, elem, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      for (int i = 0; i < 8; ++i) acc[i] += (double)v[i];
     }
   }
 #pragma unroll
@@ -100,40 +104,46 @@ __global__ __launch_bounds__(256) void pool_kernel(
   __syncthreads();
   if (threadIdx.x < kHeadDim) {
     const int d = threadIdx.x;
-    float sum = 0.f;
+    double sum = 0.0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += red[r][d];
-    float mean = sum / (float)nJ;
-    if (!is_v && KDT == FP_E4M3) mean *= k_scale[h];
+    // e4m3: the codes' sum times the head's scale (each code times the scale
+    // is exact in float64, so this is the sum of the decoded keys)
+    if (!is_v && KDT == FP_E4M3) sum *= (double)k_scale[h];
+    const double mean = sum / (double)nJ;
     const int64_t o = ((int64_t)h * num_blocks + gb) * kHeadDim + d;
     if (is_v) {
       v_mean[o] = mean;
     } else {
-      // the fp32 mean rounded to bf16 for the discovery MFMA
       k_mean[o] = mean;
-      const __bf16 hi = f32_to_bf16(mean);
-      k_mean_bf16[o] = __builtin_bit_cast(u16, hi);
-      // squared norms of the rounding residual (exact: hi is within a bf16
-      // half-ulp of mean) and of hi, summed over the 128 dims (two waves)
-      const float r = mean - (float)hi;
-      const float hf = (float)hi;
-      const float r2 = wave_sum(r * r), h2 = wave_sum(hf * hf);
-      if ((d & 63) == 0) nred[d >> 6] = make_float2(r2, h2);
+      // kbar rounded to bf16 (once, from the float64 mean) for the
+      // discovery MFMA, and the squared norms of its rounding residual
+      // (exact: the residual of a nearest rounding is representable) and
+      // of the rounded value, summed over the 128 dims (two waves)
+      const u16 hb = f64_to_bf16_bits(mean);
+      k_mean_bf16[o] = hb;
+      const double hv = (double)bf16_bits_to_f32(hb);
+      const double r = mean - hv;
+      const double r2 = wave_sum_d(r * r), h2 = wave_sum_d(hv * hv);
+      if ((d & 63) == 0) nred[d >> 6] = make_double2(r2, h2);
     }
   }
   if (!is_v) {  // uniform per workgroup
     __syncthreads();
     if (threadIdx.x == 0) {
-      const float r2 = nred[0].x + nred[1].x, h2 = nred[0].y + nred[1].y;
-      // the factor covers the fp32 rounding of the sums and square roots
-      kres[(int64_t)h * num_blocks + gb] = (__fsqrt_rn(r2) + 0x1p-17f * __fsqrt_rn(h2)) * (1.f + 0x1p-12f);
+      const double r2 = nred[0].x + nred[1].x, h2 = nred[0].y + nred[1].y;
+      // |kbar_J - bf16(kbar_J)|_2 + kAccumRel |bf16(kbar_J)|_2, rounded up
+      // to fp32 (the factor covers the float64 sums, square roots and the
+      // final rounding)
+      const double b = (sqrt(r2) + kAccumRel * sqrt(h2)) * (1.0 + 0x1p-40);
+      kres[(int64_t)h * num_blocks + gb] = (float)b * (1.f + 0x1p-22f);
     }
   }
 }
 
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
-                       float* k_mean, float* v_mean, u16* k_mean_bf16, float* kres,
+                       double* k_mean, double* v_mean, u16* k_mean_bf16, float* kres,
                        hipStream_t st) {
   dim3 grid((unsigned)g.num_blocks, (unsigned)g.hkv, 2);
 #define FP_POOL(KD, VD)                                                                       \

@@ -424,14 +424,9 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
 
 template <int QDT>
 hipError_t launch_scores_t(const ScoresArgs& a, dim3 grid, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)scores_kernel<QDT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)kScoresSmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> smem_set;
+  const hipError_t e = set_smem_limit(smem_set, (const void*)scores_kernel<QDT>, kScoresSmem);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((scores_kernel<QDT>), grid, dim3(64 * kWaves), kScoresSmem, st, a);
   return hipGetLastError();
 }

@@ -12,8 +12,9 @@
 //           k_mean by the whole workgroup, with the row maximum re-evaluated
 //           the same way, so that every decision matches exact arithmetic.
 //   scan    one workgroup: exclusive prefix sum of the counts -> row_ptr.
-//   compact one wave per row: wavefront ballot + popcount prefix writes the
-//           kept block indices in ascending order.
+//   compact one wave per row (kRowsPerWg rows per workgroup): wavefront
+//           ballot + popcount prefix writes the kept block indices in
+//           ascending order.
 #include "fp_internal.hpp"
 
 namespace fp {
@@ -23,12 +24,17 @@ namespace {
 // Fast-path error budget (natural-log units).  The discovery logits use the
 // pooled keys rounded to bf16; the scores pass bounds, per score row, how far
 // that rounding and the fp32 accumulation of the dot products can move any
-// entry (E, stored after the scores).  kGuard adds an allowance for the fp32
-// statistics (exp2 / log2 / sums, below 1e-4 on these scales).  An entry and
-// the row max can each be off by E + kGuard / 2, so every entry within
-// guard = 2 E + kGuard of the threshold (and every candidate within guard of
-// the row max) is re-evaluated in float64; all other decisions are certain.
-constexpr float kGuard = 2e-3f;
+// entry from its exact value (E, stored after the scores).  The fp32
+// statistics (logit scaling, exp2 / log2, sums over at most 2048 rows and the
+// merges) add an absolute error below 1e-4 plus a relative one below 2^-19
+// of the score's magnitude; kStatAbs / kStatRel allow several times that.
+// An entry l and the row max lmax are therefore each within
+// E + stat(l) of exact, stat(x) = kStatAbs + kStatRel |x|, and every entry
+// within guard = 2 E + stat(l) + stat(lmax) of the threshold (and every
+// candidate within the same guard of the row max) is re-evaluated in
+// float64; all other decisions are certain.
+constexpr float kStatAbs = 1e-3f;
+constexpr float kStatRel = 0x1p-17f;
 constexpr int kRowsPerWg = 4;
 
 constexpr int kSelThreads = 256;
@@ -60,14 +66,14 @@ __device__ __forceinline__ void q_chunk8(const void* q, int64_t e0, int c, doubl
   }
 }
 
-// Exact scores of nb <= kBatch pooled keys (fp32 kbar rows staged in LDS at
-// kbs[b * 128 ..]) for the rows of (h, block I), in one pass over the query
-// rows: ex[b] = ln sum_r exp(x_rb - ref) + ref, x_rb = scale * q_r . kbar_b,
-// all in float64.  Thread t takes rows t, t + 256, ...; each query row is read
+// Exact scores of nb <= kBatch pooled keys (float64 kbar rows staged in LDS
+// at kbs[b * 128 ..]) for the rows of (h, block I), in one pass over the
+// query rows: ex[b] = ln sum_r exp(x_rb - ref) + ref, x_rb = scale * q_r .
+// kbar_b, all in float64.  Thread t takes rows t, t + 256, ...; each query row is read
 // once for all nb keys (two accumulators per key).  Called uniformly by every
 // thread; every thread returns the same ex[].
 template <int QDT>
-__device__ void exact_scores(const void* q, const float* q_scale, const float* kbs, int nb, int hq,
+__device__ void exact_scores(const void* q, const float* q_scale, const double* kbs, int nb, int hq,
                              int group, int h, int64_t tok0, int nI, double scale, double ref,
                              double (*red)[kBatch], double* ex) {
   const int R = group * nI;
@@ -94,16 +100,16 @@ __device__ void exact_scores(const void* q, const float* q_scale, const float* k
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         if (b < nb) {
-          const float4 k0 = *reinterpret_cast<const float4*>(kbs + koff + b * kHeadDim + 8 * c);
-          const float4 k1 = *reinterpret_cast<const float4*>(kbs + koff + b * kHeadDim + 8 * c + 4);
-          d0[b] = fma(v[0], (double)k0.x, d0[b]);
-          d1[b] = fma(v[1], (double)k0.y, d1[b]);
-          d0[b] = fma(v[2], (double)k0.z, d0[b]);
-          d1[b] = fma(v[3], (double)k0.w, d1[b]);
-          d0[b] = fma(v[4], (double)k1.x, d0[b]);
-          d1[b] = fma(v[5], (double)k1.y, d1[b]);
-          d0[b] = fma(v[6], (double)k1.z, d0[b]);
-          d1[b] = fma(v[7], (double)k1.w, d1[b]);
+          const double2* kp = reinterpret_cast<const double2*>(kbs + koff + b * kHeadDim + 8 * c);
+          const double2 k0 = kp[0], k1 = kp[1], k2 = kp[2], k3 = kp[3];
+          d0[b] = fma(v[0], k0.x, d0[b]);
+          d1[b] = fma(v[1], k0.y, d1[b]);
+          d0[b] = fma(v[2], k1.x, d0[b]);
+          d1[b] = fma(v[3], k1.y, d1[b]);
+          d0[b] = fma(v[4], k2.x, d0[b]);
+          d1[b] = fma(v[5], k2.y, d1[b]);
+          d0[b] = fma(v[6], k3.x, d0[b]);
+          d1[b] = fma(v[7], k3.y, d1[b]);
         }
       }
     }
@@ -145,9 +151,9 @@ __device__ void exact_scores(const void* q, const float* q_scale, const float* k
 template <int QDT>
 __global__ __launch_bounds__(kSelThreads) void decide_kernel(
     SeqMap m, int hq, int kvdiv, int group, int64_t num_blocks, int64_t num_qblocks,
-    int max_blocks, float softmax_scale,
+    int max_blocks, double softmax_scale,
     const void* __restrict__ q, const float* __restrict__ q_scale,
-    const float* __restrict__ k_mean, const float* __restrict__ scores,
+    const double* __restrict__ k_mean, const float* __restrict__ scores,
     const float* __restrict__ errb, float alpha, int n_sink,
     int n_local, uint32_t* __restrict__ keep_bits, int32_t* __restrict__ counts) {
   constexpr int kW = kMaxBlocksPerSeq / 32;
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   __shared__ float redf[kSelThreads / 64];
   __shared__ int redi[kSelThreads / 64];
   __shared__ double redd[kSelThreads / 64][kBatch];
-  __shared__ __attribute__((aligned(16))) float kbs[kBatch * kHeadDim];
+  __shared__ __attribute__((aligned(16))) double kbs[kBatch * kHeadDim];
   __shared__ int bj[kBatch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   for (int w = 1; w < kSelThreads / 64; ++w) lmax = fmaxf(lmax, redf[w]);
   const float lna = __logf(alpha);
   const float thr = lna + lmax;
-  const float guard = kGuard + 2.f * errb[row];
+  const float guard0 = 2.f * errb[row] + kStatAbs + kStatRel * fabsf(lmax);
 
   // pass 1: fast decisions and candidate bitmaps
   int need_l = 0;
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
     if (J < ncols) {
       const float l = L[J];
       const bool forced = J < n_sink || I - J < n_local;
+      const float guard = guard0 + kStatAbs + kStatRel * fabsf(l);
       kp = forced || l >= thr;
       ct = !forced && fabsf(l - thr) <= guard;
       cm = l >= lmax - guard;
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
     const int64_t tok0 = qb.tok0;
     // list owner h: rows of its query heads h * group .. (group of them),
     // pooled keys of its KV head h / kvdiv
-    const float* kb = k_mean + ((int64_t)(h / kvdiv) * num_blocks + qb.kb0) * kHeadDim;
+    const double* kb = k_mean + ((int64_t)(h / kvdiv) * num_blocks + qb.kb0) * kHeadDim;
     const double ref = (double)lmax;
     const double lnalpha = log((double)alpha);
     for (int w = tid; w < nw_row; w += kSelThreads) keep_fix[w] = 0u;
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
         kbs[e] = kb[(int64_t)bj[e / kHeadDim] * kHeadDim + e % kHeadDim];
       __syncthreads();
       double ex[kBatch];
-      exact_scores<QDT>(q, q_scale, kbs, nb, hq, group, h, tok0, nI, (double)softmax_scale, ref,
+      exact_scores<QDT>(q, q_scale, kbs, nb, hq, group, h, tok0, nI, softmax_scale, ref,
                         redd, ex);
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
@@ -456,7 +463,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (tid == 0) row_ptr[nrows] = carry_s;
 }
 
-__global__ __launch_bounds__(256) void compact_kernel(int64_t nrows, int max_blocks,
+// kRowsPerWg rows per workgroup, one wave each.
+__global__ __launch_bounds__(64 * kRowsPerWg) void compact_kernel(int64_t nrows, int max_blocks,
                                                       const uint32_t* __restrict__ keep_bits,
                                                       const int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx) {
@@ -479,6 +487,8 @@ __global__ __launch_bounds__(256) void compact_kernel(int64_t nrows, int max_blo
   }
 }
 
+unsigned compact_grid(int64_t nrows) { return (unsigned)((nrows + kRowsPerWg - 1) / kRowsPerWg); }
+
 }  // namespace
 
 hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float* scores, int mode,
@@ -486,13 +496,10 @@ hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float*
                                 int32_t* counts, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
   const unsigned nwg = (unsigned)g.num_rows;
   const size_t shm = sizeof(RankSmem);
-  static bool attr_set[2] = {false, false};
+  static std::atomic<uint64_t> smem_set[2];
   const void* fn = mode == 0 ? (const void*)rank_kernel<0> : (const void*)rank_kernel<1>;
-  if (!attr_set[mode]) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    attr_set[mode] = true;
-  }
+  const hipError_t ea = set_smem_limit(smem_set[mode], fn, shm);
+  if (ea != hipSuccess) return ea;
   if (mode == 0)
     hipLaunchKernelGGL(rank_kernel<0>, dim3(nwg), dim3(kRankThreads), shm, st, m, g.num_qblocks,
                        g.max_blocks, scores, top_k, top_p, n_sink, n_local, keep_bits, counts);
@@ -504,19 +511,19 @@ hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float*
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, g.num_rows, row_ptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_kernel, dim3(nwg), dim3(256), 0, st, g.num_rows, g.max_blocks,
-                     keep_bits, row_ptr, col_idx);
+  hipLaunchKernelGGL(compact_kernel, dim3(compact_grid(g.num_rows)), dim3(64 * kRowsPerWg), 0, st,
+                     g.num_rows, g.max_blocks, keep_bits, row_ptr, col_idx);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
-                         const float* k_mean, const float* scores, float alpha, int n_sink,
+                         const double* k_mean, const float* scores, float alpha, int n_sink,
                          int n_local, uint32_t* keep_bits, int32_t* counts, int32_t* row_ptr,
                          int32_t* col_idx, hipStream_t st) {
   const unsigned nwg = (unsigned)g.num_rows;
 #define FP_DEC(QD)                                                                              \
   hipLaunchKernelGGL((decide_kernel<QD>), dim3(nwg), dim3(kSelThreads), 0, st, m, g.hq, g.kvdiv, \
-                     g.lgroup, g.num_blocks, g.num_qblocks, g.max_blocks, g.softmax_scale, q,  \
+                     g.lgroup, g.num_blocks, g.num_qblocks, g.max_blocks, g.softmax_scale_d, q,  \
                      q_scale, k_mean, scores, scores + g.num_rows * (int64_t)g.max_blocks, alpha, \
                      n_sink, n_local, keep_bits, counts)
   if (g.qk_dtype == FP_BF16) FP_DEC(FP_BF16);
@@ -529,8 +536,8 @@ hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, cons
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, g.num_rows, row_ptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_kernel, dim3(nwg), dim3(256), 0, st, g.num_rows, g.max_blocks,
-                     keep_bits, row_ptr, col_idx);
+  hipLaunchKernelGGL(compact_kernel, dim3(compact_grid(g.num_rows)), dim3(64 * kRowsPerWg), 0, st,
+                     g.num_rows, g.max_blocks, keep_bits, row_ptr, col_idx);
   return hipGetLastError();
 }
 

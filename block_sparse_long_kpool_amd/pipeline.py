@@ -81,8 +81,9 @@ class Pipeline:
         N, NQ = p.num_blocks, p.num_query_blocks
         hkv, T, hq = db.num_kv_heads, p.total_tokens, db.num_q_heads
         f32 = torch.float32
-        self.k_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
-        self.v_mean = torch.empty((hkv, N, 128), dtype=f32, device=dev)
+        # pooled means, float64 (exact block means up to float64 rounding)
+        self.k_mean = torch.empty((hkv, N, 128), dtype=torch.float64, device=dev)
+        self.v_mean = torch.empty((hkv, N, 128), dtype=torch.float64, device=dev)
         # score rows per index-list owner (KV head, or query head with head_lists),
         # then one error bound per score row (scores_err)
         nsc = p.list_owners * NQ * p.max_blocks

@@ -48,7 +48,7 @@
  *                  s lives at page page_table[s][p / page_size], slot
  *                  p % page_size (FlashPrefill V2 article, paged KV section:
  *                  page base from the table plus in-page offset).
- *       k_mean, v_mean [Hkv, N, 128] float32 (key block J of sequence s at
+ *       k_mean, v_mean [Hkv, N, 128] float64 (key block J of sequence s at
  *                  row kboff_s + J, kboff_s = sum of nk over earlier
  *                  sequences)
  *       block_scores   [Lo, NQ, n_max] float32 (query block I of sequence s
@@ -132,7 +132,10 @@ typedef struct {
 } fp_problem;
 
 /* Supported dtype combinations (qk, v): (F32, F32), (BF16, BF16), (E4M3, BF16);
- * out_dtype F32 or BF16 with any of them.  Longest sequence <= 8192 blocks. */
+ * out_dtype F32 or BF16 with any of them.  Longest sequence <= 8192 blocks.
+ * row_ptr / col_idx offsets are int32, so Lo times the number of causal
+ * blocks of the query blocks (fp_csr_capacity) must not exceed INT32_MAX;
+ * larger batches are rejected with FP_ERR_UNSUPPORTED by every call. */
 
 /* ---- size queries (host only, read cu_seqlens_host / ctx_lens_host) ---- */
 int64_t fp_num_blocks(const fp_problem* p);       /* N = sum_s nk_s (pooled rows) */
@@ -143,7 +146,8 @@ int64_t fp_scores_elems(const fp_problem* p);     /* Lo * NQ * (n_max + 1): the
                                                      scores, then one error bound
                                                      per score row               */
 int64_t fp_csr_capacity(const fp_problem* p);     /* Lo * sum over query blocks of
-                                                     (I + 1): every causal block kept */
+                                                     (I + 1): every causal block kept
+                                                     (<= INT32_MAX)               */
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which);
 const char* fp_status_string(int32_t status);
 const char* fp_last_error(void);
@@ -154,7 +158,8 @@ const char* fp_last_error(void);
  * Pooling (FlashPrefill summary "长上下文加速 28 倍", 3.1 key pooling; V2 paper
  * reading 4.1): k_mean[h][kboff_s + J] = mean of the keys of block J of
  * sequence s for KV head h (n_J = tokens actually in the block); v_mean the
- * same for values.
+ * same for values.  The means are summed and divided in float64, i.e. they
+ * are the exact block means of the stored values up to float64 rounding.
  *
  * Scores (same summary, 3.1 query pooling + global re-weighting): for list
  * owner h (KV head h; with head_lists, query head h) and query block I, let
@@ -168,19 +173,24 @@ const char* fp_last_error(void);
  * block is a subtraction of max_J of this value (done by fp_select).
  * Entries with J > I are left unspecified.
  *
- * The dot products run on bf16 MFMA with kbar rounded to bf16 (fp32
- * accumulation).  After the Lo * NQ * n_max scores, block_scores holds one
- * float per score row (same row order): a bound E on |fast - exact| for
- * every entry of the row, E = softmax_scale * max_r |q_r|_2 *
- * max_{J<=I} (|kbar_J - bf16(kbar_J)|_2 + 2^-17 |bf16(kbar_J)|_2)
- * (Cauchy-Schwarz on the rounding of kbar, plus the fp32 accumulation of 128
- * exact products; |q_r| includes q_scale for e4m3), which fp_select uses.
+ * The dot products run on bf16 MFMA with kbar rounded (once) to bf16 and
+ * fp32 accumulation.  After the Lo * NQ * n_max scores, block_scores holds
+ * one float per score row (same row order): a bound E on how far the dot
+ * products can move any entry of the row from exact arithmetic,
+ *     E = softmax_scale * max_r |q_r|_2 *
+ *         max_{J<=I} (|kbar_J - bf16(kbar_J)|_2 + 2^-15 |bf16(kbar_J)|_2)
+ * (Cauchy-Schwarz on the rounding of the exact mean kbar_J, plus twice the
+ * worst case of an fp32 sum of 128 exact products with any faithful
+ * rounding; |q_r| includes q_scale for e4m3; a log-sum-exp over rows moves
+ * by at most its largest shift), which fp_select uses.  The fp32 statistics
+ * (exp2 / log2 / sums) add an absolute error below 1e-4 and a relative one
+ * below 2^-19 of |L| on top of E.
  *
  * q, k_cache, v_cache: inputs (layouts above).  k_mean, v_mean, block_scores:
  * outputs.  ws: FP_WS_DISCOVER workspace.
  */
 int fp_discover(const fp_problem* p, const void* q, const void* k_cache,
-                const void* v_cache, float* k_mean, float* v_mean,
+                const void* v_cache, double* k_mean, double* v_mean,
                 float* block_scores, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -196,17 +206,22 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache,
  * Kept indices are written ascending (compaction, same summary 3.3).
  *
  * Because block_scores comes from a bf16 fast path, every entry whose fast
- * value lies within 2 E + 2e-3 (natural-log units; E = the row's bound
- * stored after the scores, 2e-3 an allowance for the fp32 statistics) of the
- * threshold, together with the row's candidates for the maximum, is
- * re-evaluated from q and k_mean in float64 before it is decided; every
- * other decision is the same as in exact arithmetic.
+ * value lies within 2 E + stat(l) + stat(lmax) of the threshold (E = the
+ * row's bound stored after the scores, stat(x) = 1e-3 + 2^-17 |x| an
+ * allowance of several times the fp32 statistics' error, l the entry and
+ * lmax the row maximum, natural-log units), together with the row's
+ * candidates for the maximum (within the same guard of it), is re-evaluated
+ * in float64 from q and the float64 means k_mean before it is decided.
+ * Every other decision follows from the bound.  So the lists equal those of
+ * exact arithmetic on the stored q and the exact block means, except for
+ * entries whose exact normalised score is within float64 rounding (about
+ * 1e-12 relative) of alpha.
  *
  * q, k_mean, block_scores: inputs from the same problem.  row_ptr
  * [fp_num_rows + 1], col_idx [col_capacity]: outputs.  col_capacity must be
  * >= fp_csr_capacity(p).  ws: FP_WS_SELECT workspace.
  */
-int fp_select(const fp_problem* p, const void* q, const float* k_mean,
+int fp_select(const fp_problem* p, const void* q, const double* k_mean,
               const float* block_scores, float alpha, int32_t sink_tokens,
               int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx,
               int64_t col_capacity, void* ws, size_t ws_bytes, void* stream);
@@ -284,8 +299,8 @@ int fp_select_topp(const fp_problem* p, const float* block_scores, float top_p,
  */
 int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* row_ptr,
-                         const int32_t* col_idx, const float* k_mean,
-                         const float* v_mean, int32_t mean_correction, void* out,
+                         const int32_t* col_idx, const double* k_mean,
+                         const double* v_mean, int32_t mean_correction, void* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

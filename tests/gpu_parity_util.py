@@ -9,7 +9,6 @@ import time
 import numpy as np
 
 from oracle import BAND_REL, OracleProblem, pooled_all, run_pipeline
-from oracle.flashprefill import bf16_round
 
 # Output tolerances (max-abs vs the fp64 oracle fed the GPU's own lists).
 TOL_OUT = {"bf16": 2e-2, "f32": 2e-2, "e4m3": 6e-2}
@@ -24,24 +23,42 @@ TOL_LSE = 5e-2
 # is bounded by score_bound() below (rounding + accumulation); the fp32
 # statistics (exp2, sums, log) add less than TOL_SCORE_STATS.
 TOL_SCORE_STATS = 1e-3
+# pooled means: float64 sums of the stored values and one division, on both
+# sides (relative to max(1, |mean|))
+TOL_POOL = 1e-12
+# fp32 accumulation allowance of a 128-term dot product of exact products
+ACCUM_REL = 2.0 ** -15
+
+
+def bf16_round64(x):
+    """float64 -> nearest bfloat16 (ties to even), as float64: the grid
+    spacing in the binade of |x| is 2^(e-7); dividing by it is exact and
+    numpy's rint rounds half to even.  (Finite values in the bf16 range.)"""
+    v = np.asarray(x, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex.astype(np.int64) - 1, -126)
+    quantum = np.ldexp(1.0, (e - 7).astype(np.int32))
+    r = np.rint(a / quantum) * quantum
+    return np.where(a == 0, v, np.copysign(r, v))
 
 
 def score_bound(prob, k_mean, h, s, I):
     """Bound on |fast - exact| block score of row (h, s, I), derived from the
-    fast path's arithmetic: rounding kbar_J to bf16 moves x_rJ by at most
-    scale |q_r| |kbar_J - bf16(kbar_J)| (Cauchy-Schwarz), and fp32
-    accumulation of 128 exact products by at most scale |q_r| 2^-17
+    fast path's arithmetic: rounding the exact mean kbar_J to bf16 moves x_rJ
+    by at most scale |q_r| |kbar_J - bf16(kbar_J)| (Cauchy-Schwarz), and fp32
+    accumulation of 128 exact products by at most scale |q_r| ACCUM_REL
     |bf16(kbar_J)|; a log-sum-exp over rows moves by at most the largest
-    shift.  k_mean: the library's fp32 pooled keys (checked against the
-    oracle separately)."""
+    shift.  k_mean: float64 pooled keys (the library's, checked against the
+    oracle's separately, or the oracle's own)."""
     B = prob.block_size
     nI = min(B, prob.seqlen(s) - I * B)
     qg = prob.queries(s, prob.list_heads(h), I * B + np.arange(nI)).reshape(-1, prob.d)
     qn = float(np.sqrt((qg * qg).sum(1)).max())
     kb0 = int(prob.block_offsets()[s])
     km = k_mean[prob.list_kv_head(h), kb0:kb0 + I + 1].astype(np.float64)
-    hi = bf16_round(km)
-    res = np.sqrt(((km - hi) ** 2).sum(1)) + 2.0 ** -17 * np.sqrt((hi * hi).sum(1))
+    hi = bf16_round64(km)
+    res = np.sqrt(((km - hi) ** 2).sum(1)) + ACCUM_REL * np.sqrt((hi * hi).sum(1))
     return prob.scale * qn * float(res.max())
 
 
@@ -86,7 +103,7 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
         km, vm, _ = pooled_all(prob)
         for name, ref in (("k_mean", km), ("v_mean", vm)):
             err = np.abs(g[name] - ref)
-            assert np.all(err <= 1e-5 * np.maximum(1.0, np.abs(ref))), \
+            assert np.all(err <= TOL_POOL * np.maximum(1.0, np.abs(ref))), \
                 f"{name}: max err {err.max():.3g}"
     res = run_pipeline(prob, alpha, sinks, local, correction, rows=rows,
                        given_csr=(g["row_ptr"], g["col_idx"]))
@@ -132,6 +149,55 @@ def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
     assert stats["out_err"] <= TOL_OUT[spec.qk_dtype], stats
     assert stats["lse_err"] <= TOL_LSE, stats
     return stats
+
+
+def oracle_scores_all_rows(w, head_lists=False, threads=16):
+    """The oracle's block scores L of every (owner, s, I) row of the
+    workload (float64), computed once per workload and shared by every
+    alpha (the scores do not depend on it).  List owners run in parallel
+    threads (numpy releases the GIL in its products and exponentials)."""
+    from concurrent.futures import ThreadPoolExecutor
+    prob = OracleProblem.from_workload(w)
+    prob.head_lists = head_lists
+    owners = list(range(prob.list_owners))
+
+    def one(h):
+        rows = [(h, s, I) for s in range(prob.num_seqs) for I in prob.query_blocks(s)]
+        res = run_pipeline(prob, 1.0, rows=rows, attend=False)
+        return {k: r["L"] for k, r in res.items()}
+
+    t0 = time.time()
+    out = {}
+    with ThreadPoolExecutor(min(threads, len(owners))) as ex:
+        for part in ex.map(one, owners):
+            out.update(part)
+    log(f"  oracle scores of {len(out)} rows in {time.time() - t0:.1f} s")
+    return prob, out
+
+
+def compare_lists_all_rows(prob, scores, rp, ci, alpha, sinks=256, local=512):
+    """Every row's GPU list against the oracle's selection from its float64
+    scores: identical outside the oracle's 1e-5 band at the threshold.
+    Returns (rows, in-band entries, mismatches); raises on a mismatch."""
+    from oracle import select_row
+    band = mism = 0
+    bad = []
+    B = prob.block_size
+    for (h, s, I), L in scores.items():
+        kept, bflag = select_row(L, I, alpha, sinks, local, B)
+        row = prob.row_index(h, s, I)
+        got = ci[rp[row]:rp[row + 1]]
+        if np.any(np.diff(got) <= 0):
+            bad.append(("order", h, s, I))
+        fl = set(np.nonzero(bflag)[0].tolist())
+        band += len(fl)
+        d = (set(got.tolist()) ^ set(kept.tolist())) - fl
+        if d:
+            mism += len(d)
+            bad.append((h, s, I, sorted(d)[:4]))
+    log(f"  lists alpha={alpha}: {len(scores)} rows, {band} in band, {mism} mismatches")
+    assert not bad, bad[:8]
+    return len(scores), band, mism
 
 
 def sample_rows(w, n_per_head, seed=0, head_lists=False):

@@ -155,3 +155,22 @@ def test_size_queries_per_query_head_lists(bind):
     bad.c.head_lists = 2
     with pytest.raises(bind.FpError, match="head_lists"):
         bad.num_rows
+
+
+def test_csr_beyond_int32_offsets_is_rejected(bind):
+    """row_ptr / col_idx offsets are int32: a batch whose every-causal-block
+    capacity exceeds INT32_MAX is refused by the size queries and by every
+    call before any launch (two 1M-token prompts with one list per query
+    head: 2 x 32 x 8192 x 8193 / 2 entries).  Just below the limit it is
+    accepted."""
+    big = _problem(bind, seqlens=(8192 * 128, 8192 * 128), hq=32, hkv=4, page=128,
+                   head_lists=True)
+    with pytest.raises(bind.FpError, match="int32"):
+        _ = big.csr_capacity
+    lib = bind.load_library()
+    assert lib.fp_discover(big.ref, 1, 1, 1, 1, 1, 1, 256, 1 << 30, None) == -2
+    assert lib.fp_select(big.ref, 1, 1, 1, 0.1, 256, 512, 1, 1, 1 << 40, 256, 1 << 30, None) == -2
+    assert lib.fp_sparse_attn_paged(big.ref, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, 256,
+                                    1 << 30, None) == -2
+    ok = _problem(bind, seqlens=(8192 * 128, 8192 * 128), hq=32, hkv=4, page=128)
+    assert ok.csr_capacity == 2 * 4 * 8192 * 8193 // 2 < 2 ** 31 - 1
