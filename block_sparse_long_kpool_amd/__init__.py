@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     Problem,
     fp_discover,
     fp_select,
+    fp_select_noalloc,
     fp_select_topk,
     fp_select_topp,
     fp_sparse_attn_paged,

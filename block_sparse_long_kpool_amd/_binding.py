@@ -22,7 +22,8 @@ EXPORTED = (
     "fp_num_blocks", "fp_num_query_blocks", "fp_max_blocks", "fp_num_rows", "fp_scores_elems",
     "fp_csr_capacity",
     "fp_workspace_bytes", "fp_status_string", "fp_last_error",
-    "fp_discover", "fp_select", "fp_select_topk", "fp_select_topp", "fp_sparse_attn_paged",
+    "fp_discover", "fp_select", "fp_select_noalloc", "fp_select_topk", "fp_select_topp",
+    "fp_sparse_attn_paged",
 )
 
 
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp_last_error": (ctypes.c_char_p, []),
         "fp_discover": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "fp_select": (ctypes.c_int, [P, vp, vp, vp, f32, i32, i32, vp, vp, i64, vp, sz, vp]),
+        "fp_select_noalloc": (ctypes.c_int, [P, vp, vp, vp, f32, i32, i32, vp, vp, i64, vp]),
         "fp_select_topk": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, sz, vp]),
         "fp_select_topp": (ctypes.c_int, [P, vp, f32, i32, i32, vp, vp, i64, vp, sz, vp]),
         "fp_sparse_attn_paged": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
@@ -239,6 +241,15 @@ def fp_select(p: Problem, q, k_mean, block_scores, alpha: float, sink_tokens: in
                            int(sink_tokens), int(local_tokens), _ptr(row_ptr), _ptr(col_idx),
                            col_idx.numel(), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)))
+
+
+def fp_select_noalloc(p: Problem, q, k_mean, block_scores, alpha: float, sink_tokens: int,
+                      local_tokens: int, row_ptr, col_idx, stream=None):
+    """fp_select with the library's static scratch instead of a workspace."""
+    _check(p.lib.fp_select_noalloc(p.ref, _ptr(q), _ptr_f64(k_mean), _ptr(block_scores),
+                                   float(alpha), int(sink_tokens), int(local_tokens),
+                                   _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                   _stream(stream)))
 
 
 def fp_select_topk(p: Problem, block_scores, top_k: int, sink_tokens: int, local_tokens: int,

@@ -291,6 +291,74 @@ int fp_select(const fp_problem* p, const void* q, const double* k_mean, const fl
                     "select");
 }
 
+// ---- fp_select_noalloc: fp_select with its workspace in a static device
+// array, for callers that cannot allocate device memory -------------------
+
+namespace {
+
+// Scratch of fp_select_noalloc: one copy per device (the code object's
+// device globals are instantiated on every device that loads the library)
+// until the process ends.  Holds the select workspace: block offsets, the
+// keep bitmask (4 bytes per 32 blocks per CSR row) and the row counts.
+constexpr size_t kSelectScratchBytes = size_t(8) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; host code never uses the
+// array's own name as an address (that is a host-side stand-in).
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FP_ERR_UNSUPPORTED, "fp_select_noalloc: device %d beyond the %d devices it tracks", dev,
+                kMaxDevices);
+  uintptr_t v = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!v) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    v = reinterpret_cast<uintptr_t>(ptr);
+    g_scratch_addr[dev].store(v, std::memory_order_release);  // racing threads store the same value
+  }
+  *out = reinterpret_cast<void*>(v);
+  return FP_OK;
+}
+
+}  // namespace
+
+int fp_select_noalloc(const fp_problem* p, const void* q, const double* k_mean,
+                      const float* block_scores, float alpha, int32_t sink_tokens,
+                      int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx,
+                      int64_t col_capacity, void* stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st) return st;
+  const size_t need = ws_layout(g, FP_WS_SELECT, nullptr, nullptr);
+  if (need > kSelectScratchBytes)
+    return fail(FP_ERR_WORKSPACE,
+                "fp_select_noalloc: this batch needs %zu bytes of select workspace, the static "
+                "scratch holds %zu (call fp_select with a workspace instead)",
+                need, kSelectScratchBytes);
+  if (!q || !k_mean || !block_scores || !row_ptr || !col_idx)
+    return fail(FP_ERR_INVALID, "fp_select_noalloc: a tensor pointer is NULL");
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  // the select kernels write every word of the workspace they read (block
+  // offsets, each row's bitmask words and count), so nothing is cleared
+  return fp_select(p, q, k_mean, block_scores, alpha, sink_tokens, local_tokens, row_ptr, col_idx,
+                   col_capacity, ws, kSelectScratchBytes, stream);
+}
+
 namespace {
 int select_ranked(const fp_problem* p, const float* block_scores, int mode, int32_t top_k, float top_p,
                   int32_t sink_tokens, int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx,

@@ -227,6 +227,28 @@ int fp_select(const fp_problem* p, const void* q, const double* k_mean,
               int64_t col_capacity, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp_select_noalloc -- fp_select without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, decisions, outputs and errors as fp_select, bit-identical
+ * results; the FP_WS_SELECT workspace is instead a static device array of
+ * 8 MiB inside the library (one per device, held until the process ends;
+ * its address is looked up on the first call on each device).  A batch whose
+ * FP_WS_SELECT workspace exceeds 8 MiB is rejected with FP_ERR_WORKSPACE
+ * before anything runs (the benchmark shapes need 0.5-2 MiB: 4 bytes per 32
+ * key blocks per CSR row, plus the row counts).  Nothing is allocated or
+ * freed, and no memset is issued: the kernels overwrite everything they read
+ * from the array.  Every call on one device shares the array, so calls that
+ * can overlap on a device (on different streams, or from several threads)
+ * race and give unspecified lists; calls in one stream order are safe.
+ */
+int fp_select_noalloc(const fp_problem* p, const void* q, const double* k_mean,
+                      const float* block_scores, float alpha, int32_t sink_tokens,
+                      int32_t local_tokens, int32_t* row_ptr, int32_t* col_idx,
+                      int64_t col_capacity, void* stream);
+
+/*
  * fp_select_topk / fp_select_topp -- ranked block selection, the strategies
  * of the prior methods that the max-based threshold replaces (FlashPrefill
  * summary "长上下文加速 28 倍", section 二: top-k needs a sort, top-p a

@@ -174,3 +174,20 @@ def test_csr_beyond_int32_offsets_is_rejected(bind):
                                     1 << 30, None) == -2
     ok = _problem(bind, seqlens=(8192 * 128, 8192 * 128), hq=32, hkv=4, page=128)
     assert ok.csr_capacity == 2 * 4 * 8192 * 8193 // 2 < 2 ** 31 - 1
+
+
+def test_noalloc_select_rejects_batches_beyond_its_scratch(bind):
+    """fp_select_noalloc refuses, before touching the device, a batch whose
+    select workspace exceeds its static 8 MiB scratch (1M tokens with one
+    list per query head: 262144 rows x 1 KiB of bitmask)."""
+    p = _problem(bind, seqlens=(8192 * 128,), hq=32, hkv=4, page=128, head_lists=True)
+    assert p.workspace_bytes(bind.FP_WS_SELECT) > 8 << 20
+    lib = bind.load_library()
+    st = lib.fp_select_noalloc(p.ref, 1, 1, 1, 0.1, 256, 512, 1, 1, p.csr_capacity, None)
+    assert st == -3
+    assert b"static scratch" in lib.fp_last_error()
+    small = _problem(bind)
+    assert small.workspace_bytes(bind.FP_WS_SELECT) <= 8 << 20
+    # argument errors are reported before the device is touched as well
+    assert lib.fp_select_noalloc(small.ref, None, 1, 1, 0.1, 256, 512, 1, 1,
+                                 small.csr_capacity, None) == -1
