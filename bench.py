@@ -202,6 +202,23 @@ def time_graph(pipe, alpha, correction, steps, warmup, sinks=256, local=512):
     return dict(step_ms=e0.elapsed_time(e1) / steps, wall_ms=wall)
 
 
+def time_dense(pipe, steps, warmup):
+    """Dense causal attention steps (every causal block, the aligned dense
+    baseline) timed with HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        pipe.attend_dense()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        pipe.attend_dense()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(w, alpha, correction, budget_s=20.0, seed=0):
     """Time the fp64 oracle on a seeded sample of (kv head, query block) rows
     of the same workload, growing the sample until ~budget_s of CPU work."""
@@ -345,6 +362,10 @@ def main():
                          "cached (a multiple of 128); the step processes the rest")
     ap.add_argument("--head-lists", action="store_true",
                     help="one index list per query head instead of per KV group (ablation)")
+    ap.add_argument("--dense", action="store_true",
+                    help="also time the dense causal baseline (fp_dense_attn_paged: every causal "
+                         "block, same kernel, no lists, no correction) and report the ratio")
+    ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--graph", action="store_true",
                     help="also time whole steps replayed from one HIP graph (graph_ms_per_step)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -455,6 +476,22 @@ def main():
     if select is not None:
         line["config"]["select"] = args.select
         line["roofline"]["traffic"] = None
+    if args.dense:
+        causal_all = causal_pairs(spec.seqlens, ctx=ctx) * spec.num_q_heads
+        dms = time_dense(pipe, args.dense_steps, 1)
+        dflop = 4 * d * causal_all
+        dpeak = attn_peak(spec, causal_all, 0, False)
+        line["dense"] = {
+            "kernel": "attn_kernel (dense instance)",
+            "ms": round(dms, 3),
+            "achieved": round(dflop / (dms * 1e-3) / 1e12, 3),
+            "peak": round(dpeak, 1),
+            "unit": "TFLOP/s",
+            "frac": round(dflop / (dms * 1e-3) / 1e12 / dpeak, 4),
+            "flop_per_launch": dflop,
+            "ratio_vs_sparse_step": round(dms / t["step_ms"], 3),
+            "ratio_vs_sparse_attn": round(dms / t["attn_ms"], 3),
+        }
     if args.graph and select is None:
         tg = time_graph(pipe, args.alpha, correction, args.steps, args.warmup)
         line["graph_ms_per_step"] = round(tg["step_ms"], 4)

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     FP_E4M3,
     FP_F32,
     FP_WS_ATTN,
+    FP_WS_DENSE,
     FP_WS_DISCOVER,
     FP_WS_SELECT,
     LIB_PATH,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     fp_select_topk,
     fp_select_topp,
     fp_sparse_attn_paged,
+    fp_dense_attn_paged,
     load_library,
 )
 from .pipeline import Pipeline, upload  # noqa: F401

@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libflashprefill.so")
 
 FP_F32, FP_BF16, FP_E4M3 = 0, 1, 2
-FP_WS_DISCOVER, FP_WS_SELECT, FP_WS_ATTN = 0, 1, 2
+FP_WS_DISCOVER, FP_WS_SELECT, FP_WS_ATTN, FP_WS_DENSE = 0, 1, 2, 3
 DTYPE_CODES = {"f32": FP_F32, "bf16": FP_BF16, "e4m3": FP_E4M3}
 
 EXPORTED = (
@@ -23,7 +23,7 @@ EXPORTED = (
     "fp_csr_capacity",
     "fp_workspace_bytes", "fp_status_string", "fp_last_error",
     "fp_discover", "fp_select", "fp_select_noalloc", "fp_select_topk", "fp_select_topp",
-    "fp_sparse_attn_paged",
+    "fp_sparse_attn_paged", "fp_dense_attn_paged",
 )
 
 
@@ -90,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp_select_topk": (ctypes.c_int, [P, vp, i32, i32, i32, vp, vp, i64, vp, sz, vp]),
         "fp_select_topp": (ctypes.c_int, [P, vp, f32, i32, i32, vp, vp, i64, vp, sz, vp]),
         "fp_sparse_attn_paged": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
+        "fp_dense_attn_paged": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -272,3 +273,9 @@ def fp_sparse_attn_paged(p: Problem, q, k_cache, v_cache, row_ptr, col_idx, k_me
         p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(row_ptr), _ptr(col_idx),
         _ptr_f64(k_mean), _ptr_f64(v_mean), 1 if mean_correction else 0, _ptr(out), _ptr(lse), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def fp_dense_attn_paged(p: Problem, q, k_cache, v_cache, out, lse, ws, stream=None) -> None:
+    _check(p.lib.fp_dense_attn_paged(p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                     _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))

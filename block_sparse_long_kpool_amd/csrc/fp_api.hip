@@ -113,6 +113,15 @@ int make_geometry(const fp_problem* p, Geometry* g) {
   return FP_OK;
 }
 
+// The dense baseline has no index lists: the g query heads of a KV head
+// always share its tiles, whatever head_lists says.
+void dense_geometry(Geometry* g) {
+  g->lists = g->hkv;
+  g->lgroup = g->group;
+  g->kvdiv = 1;
+  g->num_rows = g->num_qblocks * g->lists;
+}
+
 struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; float* kres; };
 struct SelectWs { int32_t* kboff; int32_t* qboff; uint32_t* bits; int32_t* counts; };
 struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; float* opart; float* lpart; };
@@ -225,6 +234,10 @@ int64_t fp_csr_capacity(const fp_problem* p) {
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which) {
   Geometry g;
   if (make_geometry(p, &g) != FP_OK) return 0;
+  if (which == FP_WS_DENSE) {
+    dense_geometry(&g);
+    which = FP_WS_ATTN;  // same layout (the pooled copies go unused)
+  }
   return ws_layout(g, which, nullptr, nullptr);
 }
 
@@ -424,8 +437,30 @@ int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache
     return st;
   return hip_status(launch_attn(g, m, p->page_table_dev, q, k_cache, v_cache, p->q_scale_dev,
                                 p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
-                                mean_correction ? 1 : 0, out, lse, w.opart, w.lpart, s),
+                                mean_correction ? 1 : 0, out, lse, w.opart, w.lpart, s, false),
                     "attn");
+}
+
+int fp_dense_attn_paged(const fp_problem* p, const void* q, const void* k_cache,
+                        const void* v_cache, void* out, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(FP_ERR_INVALID, "fp_dense_attn_paged: a tensor pointer is NULL");
+  dense_geometry(&g);
+  if ((st = check_ws(g, FP_WS_ATTN, ws, ws_bytes))) return st;
+  AttnWs w;
+  ws_layout(g, FP_WS_ATTN, ws, &w);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const SeqMap m = seq_map(p, w.kboff, w.qboff);
+  if ((st = hip_status(launch_attn_prep(g, m, nullptr, nullptr, w.km16, w.vm16, s), "attn prep")))
+    return st;
+  return hip_status(launch_attn(g, m, p->page_table_dev, q, k_cache, v_cache, p->q_scale_dev,
+                                p->k_scale_dev, nullptr, nullptr, w.km16, w.vm16, 0, out, lse, w.opart,
+                                w.lpart, s, true),
+                    "dense attn");
 }
 
 }  // extern "C"

@@ -123,7 +123,9 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 a) {
   return uint2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
-template <int QDT, int VDT, int ODT, int NW>
+// DENSE: every causal block 0..I of the row, in order, without index lists
+// or correction (the dense causal baseline on the same kernel).
+template <int QDT, int VDT, int ODT, int NW, bool DENSE>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   static_assert(NW == kAttnWaves, "one 32-row chunk per wave");
   constexpr int RC = 8 / NW;   // 32-row chunks per wave (the workgroup always covers 256 rows)
@@ -159,9 +161,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int nI = qb.nI;
   const int64_t tok0 = qb.tok0;
   const int64_t pooled_base = (int64_t)kvh * a.num_blocks + qb.kb0;
-  const int kbeg = a.row_ptr[row];
+  const int kbeg = DENSE ? 0 : a.row_ptr[row];
   // a valid list holds at most I + 1 blocks (the LDS tile list is sized for it)
-  const int nkept = min(max(a.row_ptr[row + 1] - kbeg, 0), I + 1);
+  const int nkept = DENSE ? I + 1 : min(max(a.row_ptr[row + 1] - kbeg, 0), I + 1);
   const int64_t ptrow = (int64_t)s * a.max_pages;
 
   const int hh = 2 * pack + (wave * RC) / 4;
@@ -219,11 +221,12 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   // selection stage is always in range; out-of-range entries from other
   // producers give unspecified output but no out-of-bounds access).
   const int nwords = (I >> 5) + 1;
-  if (a.correction)
+  if (!DENSE && a.correction)
     for (int w = tid; w < nwords; w += NT) sm.kept_bits[w] = 0u;
-  for (int i = tid; i < nkept; i += NT) sm.tiles[i] = (uint16_t)min(max(a.col_idx[kbeg + i], 0), I);
+  if (!DENSE)
+    for (int i = tid; i < nkept; i += NT) sm.tiles[i] = (uint16_t)min(max(a.col_idx[kbeg + i], 0), I);
   __syncthreads();
-  if (a.correction) {
+  if (!DENSE && a.correction) {
     for (int i = tid; i < nkept; i += NT) {
       const int J = sm.tiles[i];
       atomicOr(&sm.kept_bits[J >> 5], 1u << (J & 31));
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     __syncthreads();
   }
   // wave-uniform counts: keep them in scalar registers
-  const int npooled = a.correction ? __builtin_amdgcn_readfirstlane(sm.npooled) : 0;
+  const int npooled = (!DENSE && a.correction) ? __builtin_amdgcn_readfirstlane(sm.npooled) : 0;
   const int ntiles = nkept + npooled;
   // KV split: this workgroup takes tiles [tbeg, tend) of the row's list
   // (contiguous parts balanced by tile count; all of it without a split)
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int psz = a.page_size;
   const bool small_pages = psz <= kBlock;
   const int pshift = 31 - __clz(psz);
-  auto tile_index = [&](int t) { return (int)sm.tiles[t]; };
+  auto tile_index = [&](int t) { return DENSE ? t : (int)sm.tiles[t]; };
   // page id of row `tid` of kept tile t (only threads < 128); -1 if pooled
   auto fetch_page = [&](int t) -> int {
     if (t >= tend || t >= nkept || tid >= kBlock) return -1;
@@ -848,7 +851,7 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
                        const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                        const u16* km16, const u16* vm16, int correction, void* out, float* lse,
-                       float* opart, float* lpart, hipStream_t st) {
+                       float* opart, float* lpart, hipStream_t st, bool dense) {
   AttnArgs a;
   a.m = m;
   a.page_table = page_table;
@@ -878,17 +881,24 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   a.lists = g.lists;
   a.kvdiv = g.kvdiv;
   a.packs = (g.lgroup + 1) / 2;
-  a.correction = correction;
+  a.correction = dense ? 0 : correction;
   a.softmax_scale = g.softmax_scale;
   const int64_t rows = (int64_t)g.lists * g.num_qblocks;
   const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs * a.splits);
   const size_t shm = sizeof(SharedMem);
-#define FP_ATTN(QD, VD, OD)                                                                    \
+#define FP_ATTN_D(QD, VD, OD, DN)                                                              \
   do {                                                                                         \
     static std::atomic<uint64_t> smem_set;                                                     \
-    const hipError_t ea = set_smem_limit(smem_set, (const void*)attn_kernel<QD, VD, OD, kAttnWaves>, shm); \
+    const hipError_t ea =                                                                      \
+        set_smem_limit(smem_set, (const void*)attn_kernel<QD, VD, OD, kAttnWaves, DN>, shm);   \
     if (ea != hipSuccess) return ea;                                                           \
-    hipLaunchKernelGGL((attn_kernel<QD, VD, OD, kAttnWaves>), dim3(grid), dim3(64 * kAttnWaves), shm, st, a); \
+    hipLaunchKernelGGL((attn_kernel<QD, VD, OD, kAttnWaves, DN>), dim3(grid), dim3(64 * kAttnWaves), \
+                       shm, st, a);                                                            \
+  } while (0)
+#define FP_ATTN(QD, VD, OD)                    \
+  do {                                         \
+    if (dense) FP_ATTN_D(QD, VD, OD, true);    \
+    else FP_ATTN_D(QD, VD, OD, false);         \
   } while (0)
 #define FP_ATTN_O(QD, VD)                                  \
   do {                                                     \
@@ -901,6 +911,7 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   else return hipErrorInvalidValue;
 #undef FP_ATTN_O
 #undef FP_ATTN
+#undef FP_ATTN_D
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int64_t pairs = g.total_tokens * g.hq;

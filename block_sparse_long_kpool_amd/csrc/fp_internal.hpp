@@ -314,10 +314,12 @@ hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const double* k_
 // Parts per row of the attention launch (1: no split).
 int attn_splits(const Geometry& g);
 
+// dense: every causal block of each row (no index lists, no correction;
+// row_ptr / col_idx / km16 / vm16 unused).
 hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_table, const void* q,
                        const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                        const u16* km16, const u16* vm16, int correction, void* out, float* lse,
-                       float* opart, float* lpart, hipStream_t st);
+                       float* opart, float* lpart, hipStream_t st, bool dense);
 
 }  // namespace fp

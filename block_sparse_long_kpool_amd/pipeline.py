@@ -11,8 +11,9 @@ from __future__ import annotations
 from dataclasses import dataclass
 from typing import Optional
 
-from ._binding import (FP_WS_ATTN, FP_WS_DISCOVER, FP_WS_SELECT, Problem, fp_discover,
-                       fp_select, fp_select_topk, fp_select_topp, fp_sparse_attn_paged)
+from ._binding import (FP_WS_ATTN, FP_WS_DENSE, FP_WS_DISCOVER, FP_WS_SELECT, Problem,
+                       fp_dense_attn_paged, fp_discover, fp_select, fp_select_topk,
+                       fp_select_topp, fp_sparse_attn_paged)
 
 
 @dataclass
@@ -97,6 +98,7 @@ class Pipeline:
         self.lse = torch.empty((hq, T), dtype=f32, device=dev)
         self.ws = {k: torch.empty(max(256, p.workspace_bytes(k)), dtype=torch.uint8, device=dev)
                    for k in (FP_WS_DISCOVER, FP_WS_SELECT, FP_WS_ATTN)}
+        self._dense_ws = None
 
     def discover(self, stream=None):
         d = self.db
@@ -120,6 +122,17 @@ class Pipeline:
         fp_sparse_attn_paged(self.problem, d.q, d.k_cache, d.v_cache, self.row_ptr,
                              self.col_idx, self.k_mean, self.v_mean, correction, self.out,
                              self.lse if with_lse else None, self.ws[FP_WS_ATTN], stream)
+
+    def attend_dense(self, with_lse: bool = True, stream=None):
+        """Dense causal attention over every causal block (the aligned dense
+        baseline), into the same out / lse buffers."""
+        import torch
+        if self._dense_ws is None:
+            n = max(256, self.problem.workspace_bytes(FP_WS_DENSE))
+            self._dense_ws = torch.empty(n, dtype=torch.uint8, device=self.db.q.device)
+        d = self.db
+        fp_dense_attn_paged(self.problem, d.q, d.k_cache, d.v_cache, self.out,
+                            self.lse if with_lse else None, self._dense_ws, stream)
 
     def run(self, alpha: float, sink_tokens: int = 256, local_tokens: int = 512,
             correction: bool = True, stream=None):

@@ -97,7 +97,8 @@ typedef enum {
 typedef enum {
   FP_WS_DISCOVER = 0,
   FP_WS_SELECT = 1,
-  FP_WS_ATTN = 2
+  FP_WS_ATTN = 2,
+  FP_WS_DENSE = 3
 } fp_workspace_kind;
 
 typedef struct {
@@ -324,6 +325,27 @@ int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache
                          const int32_t* col_idx, const double* k_mean,
                          const double* v_mean, int32_t mean_correction, void* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp_dense_attn_paged -- dense causal attention over the same paged cache, on
+ * the same kernel: every causal block 0..I of each query block, in order,
+ * with no index lists and no mean correction.  It is the aligned dense
+ * baseline of the sparse call (FlashPrefill V2 paper reading, section 五:
+ * the sparse operator's speed-up is quoted against a dense kernel built on
+ * the same stack; 5.3 and 5.6 state the ratios), and equals
+ * fp_sparse_attn_paged with every causal block listed and mean_correction = 0.
+ *
+ * For query head hq and query token at position p (KV head hq / (Hq / Hkv)):
+ *   out = sum_{j <= p} e^{y_j} v_j / sum_{j <= p} e^{y_j},
+ *   lse = ln sum_{j <= p} e^{y_j},  y_j = softmax_scale * q . k_j
+ * (keys of the cached prefix included).  The g query heads of a KV head are
+ * packed into shared K/V tiles whatever head_lists says.  Small launches
+ * split rows as fp_sparse_attn_paged does.  q, k_cache, v_cache: inputs;
+ * out: output; lse: output or NULL; ws: FP_WS_DENSE workspace.
+ */
+int fp_dense_attn_paged(const fp_problem* p, const void* q, const void* k_cache,
+                        const void* v_cache, void* out, float* lse, void* ws,
+                        size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

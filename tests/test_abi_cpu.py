@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("fp_discover", "fp_select", "fp_sparse_attn_paged"):
+    for n in ("fp_discover", "fp_select", "fp_sparse_attn_paged", "fp_dense_attn_paged"):
         assert n in names
 
 
@@ -61,7 +61,7 @@ def test_size_queries(bind):
     assert p.num_rows == 2 * sum(n)
     assert p.scores_elems == 2 * sum(n) * (8 + 1)  # scores + one bound per row
     assert p.csr_capacity == 2 * sum(x * (x + 1) // 2 for x in n)
-    for which in (bind.FP_WS_DISCOVER, bind.FP_WS_SELECT, bind.FP_WS_ATTN):
+    for which in (bind.FP_WS_DISCOVER, bind.FP_WS_SELECT, bind.FP_WS_ATTN, bind.FP_WS_DENSE):
         assert p.workspace_bytes(which) > 0
         assert p.workspace_bytes(which) % 256 == 0
 
@@ -191,3 +191,16 @@ def test_noalloc_select_rejects_batches_beyond_its_scratch(bind):
     # argument errors are reported before the device is touched as well
     assert lib.fp_select_noalloc(small.ref, None, 1, 1, 0.1, 256, 512, 1, 1,
                                  small.csr_capacity, None) == -1
+
+
+def test_dense_call_validation(bind):
+    """fp_dense_attn_paged: NULL tensors and a short workspace are refused
+    before any launch; its workspace does not depend on head_lists (the
+    dense kernel always packs the query heads of a KV head)."""
+    p = _problem(bind)
+    lib = bind.load_library()
+    need = p.workspace_bytes(bind.FP_WS_DENSE)
+    assert lib.fp_dense_attn_paged(p.ref, None, 1, 1, 1, None, 256, need, None) == -1
+    assert lib.fp_dense_attn_paged(p.ref, 1, 1, 1, 1, None, 256, need - 1, None) == -3
+    ph = _problem(bind, head_lists=True)
+    assert ph.workspace_bytes(bind.FP_WS_DENSE) == need
