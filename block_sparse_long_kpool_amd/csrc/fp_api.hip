@@ -122,7 +122,7 @@ void dense_geometry(Geometry* g) {
   g->num_rows = g->num_qblocks * g->lists;
 }
 
-struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; float* kres; };
+struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; float* kres; float* bnorm; };
 struct SelectWs { int32_t* kboff; int32_t* qboff; uint32_t* bits; int32_t* counts; };
 struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; float* opart; float* lpart; };
 
@@ -152,6 +152,7 @@ size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
     w.qboff = (int32_t*)take(boff_bytes);
     w.km16 = (u16*)take(pooled16);  // kbar rounded to bf16
     w.kres = (float*)take(sizeof(float) * (size_t)g.hkv * (size_t)g.num_blocks);
+    w.bnorm = (float*)take(sizeof(float) * (size_t)g.hkv * (size_t)g.num_blocks);  // |bf16 kbar|
     if (out) *reinterpret_cast<DiscoverWs*>(out) = w;
   } else if (which == FP_WS_SELECT) {
     SelectWs w;
@@ -270,9 +271,9 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const v
   const SeqMap m = seq_map(p, w.kboff, w.qboff);
   if ((st = hip_status(launch_plan(m, s), "plan"))) return st;
   if ((st = hip_status(launch_pool(g, m, p->page_table_dev, k_cache, v_cache, p->k_scale_dev,
-                                   k_mean, v_mean, w.km16, w.kres, s), "pool")))
+                                   k_mean, v_mean, w.km16, w.kres, w.bnorm, s), "pool")))
     return st;
-  return hip_status(launch_scores(g, m, q, p->q_scale_dev, w.km16, w.kres, block_scores, s),
+  return hip_status(launch_scores(g, m, q, p->q_scale_dev, w.km16, w.kres, w.bnorm, block_scores, s),
                     "scores");
 }
 

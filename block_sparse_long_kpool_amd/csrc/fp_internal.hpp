@@ -289,12 +289,13 @@ hipError_t launch_plan(const SeqMap& m, hipStream_t st);
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
                        double* k_mean, double* v_mean, u16* k_mean_bf16, float* kres,
-                       hipStream_t st);
+                       float* bnorm, hipStream_t st);
 
 // Scores [lists * NQ, max_blocks] followed by one error bound per score row.
+// bnorm: |bf16(kbar_J)|_2 per pooled key (rounded up), from the pooling pass.
 hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
-                         const u16* k_mean_bf16, const float* kres, float* scores,
-                         hipStream_t st);
+                         const u16* k_mean_bf16, const float* kres, const float* bnorm,
+                         float* scores, hipStream_t st);
 
 hipError_t launch_select(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
                          const double* k_mean, const float* scores, float alpha, int n_sink,

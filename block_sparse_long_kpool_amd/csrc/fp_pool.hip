@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
     SeqMap m, const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
     int64_t num_blocks, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ k_scale, double* __restrict__ k_mean, double* __restrict__ v_mean,
-    u16* __restrict__ k_mean_bf16, float* __restrict__ kres) {
+    u16* __restrict__ k_mean_bf16, float* __restrict__ kres, float* __restrict__ bnorm) {
   __shared__ double red[16][kHeadDim + 2];
   __shared__ double2 nred[kHeadDim / 64];
   const int gb = blockIdx.x;
@@ -137,6 +137,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
       // final rounding)
       const double b = (sqrt(r2) + kAccumRel * sqrt(h2)) * (1.0 + 0x1p-40);
       kres[(int64_t)h * num_blocks + gb] = (float)b * (1.f + 0x1p-22f);
+      bnorm[(int64_t)h * num_blocks + gb] = (float)sqrt(h2) * (1.f + 0x1p-22f);
     }
   }
 }
@@ -144,12 +145,12 @@ __global__ __launch_bounds__(256) void pool_kernel(
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
                        double* k_mean, double* v_mean, u16* k_mean_bf16, float* kres,
-                       hipStream_t st) {
+                       float* bnorm, hipStream_t st) {
   dim3 grid((unsigned)g.num_blocks, (unsigned)g.hkv, 2);
 #define FP_POOL(KD, VD)                                                                       \
   hipLaunchKernelGGL((pool_kernel<KD, VD>), grid, dim3(256), 0, st, m, page_table,            \
                      g.max_pages, g.page_size, g.hkv, g.num_blocks, k_cache,                   \
-                     v_cache, k_scale, k_mean, v_mean, k_mean_bf16, kres)
+                     v_cache, k_scale, k_mean, v_mean, k_mean_bf16, kres, bnorm)
   if (g.qk_dtype == FP_BF16 && g.v_dtype == FP_BF16) FP_POOL(FP_BF16, FP_BF16);
   else if (g.qk_dtype == FP_E4M3 && g.v_dtype == FP_BF16) FP_POOL(FP_E4M3, FP_BF16);
   else if (g.qk_dtype == FP_F32 && g.v_dtype == FP_F32) FP_POOL(FP_F32, FP_F32);

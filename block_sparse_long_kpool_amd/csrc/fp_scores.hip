@@ -21,9 +21,14 @@
 //     rows, so the MFMA operand reads are conflict-free.
 //   * X = Q . Kbar^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  In
 //     the result layout a lane owns one pooled-key column and 16 rows of each
-//     chunk: the column max and exp-sum are lane-local, lanes l and l^32 are
-//     merged with one v_permlane32_swap each, and the 8 waves through LDS
-//     once per tile.
+//     chunk: the exp-sum is lane-local, lanes l and l^32 are merged with one
+//     v_permlane32_swap, and the 8 waves through LDS once per tile.
+//   * no column max: the sums are taken against a per-column reference known
+//     before the MFMAs, softmax_scale * max_r |q_r|_2 * |bf16(kbar_J)|_2
+//     (Cauchy-Schwarz bounds every logit of the column by it), so
+//     S = sum_r exp(x_rJ - ref) <= R and L = ref + ln S; a column whose sum
+//     falls below 2^-64 (reference far above its logits) is recomputed with
+//     its true max, so the result keeps the same fp32 accuracy.
 //   * error bound instead of a second MFMA term: rounding kbar_J to bf16
 //     moves x_rJ by at most softmax_scale * |q_r|_2 * |kbar_J - bf16(kbar_J)|_2
 //     (Cauchy-Schwarz), and a log-sum-exp over rows moves by at most the
@@ -54,7 +59,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 struct ScoresSmem {
   u16 kb[2][kTerm];              // [buffer]: 64 KiB
-  float2 part[2][kWaves][kJT];   // per wave (max, sum) of each key, by buffer
+  float bn[2][kJT];              // [buffer]: |bf16(kbar_J)|_2 of the tile's keys
+  float2 part[2][kWaves][kJT];   // per wave (reference, sum) of each key, by buffer
   float red[2][kWaves];          // per wave: largest residual bound, largest row norm^2
 };
 constexpr size_t kScoresSmem = sizeof(ScoresSmem);
@@ -65,6 +71,7 @@ struct ScoresArgs {
   const float* q_scale;
   const u16* kmean16;   // kbar rounded to bf16 [Hkv, NK, 128]
   const float* kres;    // residual bound of each pooled key [Hkv, NK]
+  const float* bnorm;   // |bf16(kbar_J)|_2 of each pooled key [Hkv, NK] (rounded up)
   float* scores;
   float* errb;          // per score row: bound on the error of its entries
   int64_t num_blocks;   // NK (pooled rows per KV head)
@@ -161,40 +168,29 @@ __device__ __forceinline__ float2 column_stats(const f32x16* acc, const float* c
   return make_float2(m, pair_sum(s));
 }
 
-// Slice KK (0..7) of the column statistics of one finished 32-key chunk,
-// spread over the eight head-dim steps of the next chunk's MFMAs: slices 0-1
-// take the column max of row chunk 0 and 1 (then the lane-pair max), slices
-// 2-7 the exp-sum of the 32 (row chunk, row) elements in order, so the
-// operations and the summation order are those of column_stats.
+// Slice KK (0..7) of the column exp-sum of one finished 32-key chunk against
+// the column's reference ref (an upper bound of every logit of the column,
+// see ref_column), spread over the eight head-dim steps of the next chunk's
+// MFMAs: four of the 32 (row chunk, row) elements per slice, in order.
 template <bool MASKED, int KK>
-__device__ __forceinline__ void stats_slice(const f32x16* acc, const float* csc, const int* nval,
-                                            int half, float& m, float& s) {
-  if constexpr (KK < 2) {
-    constexpr int rc = KK;
-    float mr = -INFINITY;
+__device__ __forceinline__ void sum_slice(const f32x16* acc, const float* csc, const int* nval,
+                                          int half, float ref, float& s) {
+  if constexpr (KK == 0) s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-      mr = fmaxf(mr, (!MASKED || row < nval[rc]) ? acc[rc][i] : -INFINITY);
-    }
-    if constexpr (KK == 0) {
-      m = fmaxf(-INFINITY, mr * csc[0]);
-      s = 0.f;
-    } else {
-      m = pair_max(fmaxf(m, mr * csc[1]));
-    }
-  } else {
-    constexpr int e0 = KK == 2 ? 0 : KK == 3 ? 5 : KK == 4 ? 10 : KK == 5 ? 15 : KK == 6 ? 20 : 26;
-    constexpr int e1 = KK == 7 ? 32 : (KK == 6 ? 26 : e0 + 5);
-#pragma unroll
-    for (int e = e0; e < e1; ++e) {
-      const int rc = e >> 4, i = e & 15;
-      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-      const float x = __builtin_amdgcn_exp2f(fmaf(acc[rc][i], csc[rc], -m));
-      s += (!MASKED || row < nval[rc]) ? x : 0.f;
-    }
+  for (int e = 4 * KK; e < 4 * KK + 4; ++e) {
+    const int rc = e >> 4, i = e & 15;
+    const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+    const float x = __builtin_amdgcn_exp2f(fmaf(acc[rc][i], csc[rc], -ref));
+    s += (!MASKED || row < nval[rc]) ? x : 0.f;
   }
 }
+
+// A column's exp-sum against its reference is trusted when it is at least
+// kSumFloor: its largest term is then >= 2^-75, a normal float, and terms
+// flushed below 2^-126 change it by less than 2^-51 relatively.  Otherwise
+// (a reference far above every logit of the column, or no valid row) the
+// wave recomputes the chunk's statistics with the true column max.
+constexpr float kSumFloor = 0x1p-64f;
 
 // MFMAs of head-dim step kk of one 32-key chunk.
 __device__ __forceinline__ void mma_step(const bf16x8 (&qf)[kRC][8], int kk, bf16x8 vh,
@@ -213,43 +209,81 @@ template <bool MASKED>
 __device__ __forceinline__ float2 chunk_overlapped(const u16* bh, int jc, int col,
                                                    int half, const bf16x8 (&qf)[kRC][8],
                                                    f32x16* acc, const f32x16* prev,
-                                                   const float* csc, const int* nval) {
+                                                   const float* csc, const int* nval, float ref) {
   const int r = jc * 32 + col;
   auto opnd = [&](const u16* b, int kk) {
     return *reinterpret_cast<const bf16x8*>(b + r * kHeadDim + swz16(8 * half + kk, r) * 8);
   };
-  float m, s;
+  float s;
   bf16x8 vh = opnd(bh, 0);
-#define FP_STEP(KK)                                       \
-  {                                                       \
-    bf16x8 nh;                                            \
-    if constexpr (KK < 7) nh = opnd(bh, KK + 1);          \
-    mma_step(qf, KK, vh, acc);                            \
-    stats_slice<MASKED, KK>(prev, csc, nval, half, m, s); \
-    interleave<2, 1>();                                   \
-    __builtin_amdgcn_sched_barrier(0);                    \
-    if constexpr (KK < 7) vh = nh;                        \
+#define FP_STEP(KK)                                          \
+  {                                                          \
+    bf16x8 nh;                                               \
+    if constexpr (KK < 7) nh = opnd(bh, KK + 1);             \
+    mma_step(qf, KK, vh, acc);                               \
+    sum_slice<MASKED, KK>(prev, csc, nval, half, ref, s);    \
+    interleave<2, 1>();                                      \
+    __builtin_amdgcn_sched_barrier(0);                       \
+    if constexpr (KK < 7) vh = nh;                           \
   }
   FP_STEP(0) FP_STEP(1) FP_STEP(2) FP_STEP(3) FP_STEP(4) FP_STEP(5) FP_STEP(6) FP_STEP(7)
 #undef FP_STEP
-  return make_float2(m, pair_sum(s));
+  return make_float2(ref, pair_sum(s));
+}
+
+// Statistics of a finished chunk against the column reference, falling back
+// to the true column max (column_stats) when any lane's sum is below
+// kSumFloor (wave-uniform branch; acc must still hold the chunk).
+template <bool MASKED>
+__device__ __forceinline__ float2 checked(float2 st, const f32x16* acc, const float* csc,
+                                          const int* nval, int half) {
+  if (__builtin_expect(__any(!(st.y >= kSumFloor)), 0)) {
+    bool rows = !MASKED;  // wave-uniform: a wave without any valid row yields (-inf, 0)
+#pragma unroll
+    for (int rc = 0; rc < kRC; ++rc) rows |= nval[rc] > 0;
+    st = rows ? column_stats<MASKED>(acc, csc, nval, half) : make_float2(-INFINITY, 0.f);
+  }
+  return st;
+}
+
+// Sum against the reference without interleaving (chunks outside the
+// pipeline), with the same fallback.
+template <bool MASKED>
+__device__ __forceinline__ float2 ref_stats(const f32x16* acc, const float* csc, const int* nval,
+                                            int half, float ref) {
+  float s;
+  sum_slice<MASKED, 0>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 1>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 2>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 3>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 4>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 5>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 6>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, 7>(acc, csc, nval, half, ref, s);
+  return checked<MASKED>(make_float2(ref, pair_sum(s)), acc, csc, nval, half);
 }
 
 // One LDS tile for this wave.  Full tiles (kJC chunks) run as one basic block
 // with two accumulator sets: chunk j+1's MFMAs overlap chunk j's statistics.
+// ref[jc]: the reference of this lane's key column in chunk jc.
 template <bool MASKED>
 __device__ __forceinline__ void tile_chunks(const u16* bh, int njc, int col,
                                             int half, const bf16x8 (&qf)[kRC][8],
-                                            const float* csc, const int* nval, float2* part) {
+                                            const float* csc, const int* nval, const float* ref,
+                                            float2* part) {
   f32x16 acc0[kRC], acc1[kRC];
   if (njc == kJC) {
     static_assert(kJC == 4, "pipeline below is written for 4 chunks per tile");
     mma_chunk(bh, 0, col, half, qf, acc0);
     __builtin_amdgcn_sched_barrier(0);
-    const float2 s0 = chunk_overlapped<MASKED>(bh, 1, col, half, qf, acc1, acc0, csc, nval);
-    const float2 s1 = chunk_overlapped<MASKED>(bh, 2, col, half, qf, acc0, acc1, csc, nval);
-    const float2 s2 = chunk_overlapped<MASKED>(bh, 3, col, half, qf, acc1, acc0, csc, nval);
-    const float2 s3 = column_stats<MASKED>(acc1, csc, nval, half);
+    // each chunk's sums are checked before its accumulators are reused
+    const float2 s0 = checked<MASKED>(chunk_overlapped<MASKED>(bh, 1, col, half, qf, acc1, acc0, csc, nval, ref[0]),
+                                      acc0, csc, nval, half);
+    const float2 s1 = checked<MASKED>(chunk_overlapped<MASKED>(bh, 2, col, half, qf, acc0, acc1, csc, nval, ref[1]),
+                                      acc1, csc, nval, half);
+    const float2 s2 = checked<MASKED>(chunk_overlapped<MASKED>(bh, 3, col, half, qf, acc1, acc0, csc, nval, ref[2]),
+                                      acc0, csc, nval, half);
+    const float2 s3 = ref_stats<MASKED>(acc1, csc, nval, half, ref[3]);
     if (half == 0) {
       part[col] = s0;
       part[32 + col] = s1;
@@ -300,6 +334,7 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
   // causal range re-read the last valid row (results unused).  The lane index
   // is made opaque here so that the source addresses are recomputed per tile
   // instead of being hoisted into live registers.
+  const float* bnbase = a.bnorm + (int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0;
   auto stage = [&](int tile, int buf) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -310,6 +345,10 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       const int J = min(tile * kJT + r, ncols - 1);
       const u16* src = kbase + (int64_t)J * kHeadDim + swz16(ln & 15, r) * 8;
       load_lds16(src, &sm.kb[buf][seg * 512]);
+    }
+    if (wave < 2) {  // the norms of the tile's 128 keys: one dword per lane
+      const int J = min(tile * kJT + 64 * wave + ln, ncols - 1);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(bnbase + J), (lds_void*)&sm.bn[buf][64 * wave], 4, 0, 0);
     }
   };
 
@@ -368,18 +407,27 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
     stage(tile0, tile0 & 1);
     wait_vm();
     __syncthreads();
+    float qp2 = 0.f;  // largest squared query-row norm of this pass
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) qn2 = fmaxf(qn2, sm.red[1][w]);
+    for (int w = 0; w < kWaves; ++w) qp2 = fmaxf(qp2, sm.red[1][w]);
+    qn2 = fmaxf(qn2, qp2);
+    // reference of a key column: softmax_scale log2(e) max_r |q_r| |bf16(kbar_J)|
+    // bounds every logit x_rJ of the pass (Cauchy-Schwarz; the margin covers
+    // the fp32 accumulation and roundings), so exp2(x_rJ - ref) <= ~1
+    const float cref = a.logit_scale * kLog2e * __fsqrt_rn(qp2) * (1.f + 0x1p-10f);
 
     for (int tile = tile0; tile < tile1; ++tile) {
       const int buf = tile & 1;
       if (tile + 1 < tile1) stage(tile + 1, buf ^ 1);
       const int njc = min(kJC, (ncols - tile * kJT + 31) >> 5);
       const u16* bh = sm.kb[buf];
+      float ref[kJC];
+#pragma unroll
+      for (int jc = 0; jc < kJC; ++jc) ref[jc] = cref * sm.bn[buf][jc * 32 + col];
       if (masked)
-        tile_chunks<true>(bh, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
+        tile_chunks<true>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
       else
-        tile_chunks<false>(bh, njc, col, half, qf, csc, nval, sm.part[buf][wave]);
+        tile_chunks<false>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
 
       wait_vm();
       __syncthreads();
@@ -434,8 +482,8 @@ hipError_t launch_scores_t(const ScoresArgs& a, dim3 grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, const float* q_scale,
-                         const u16* k_mean_bf16, const float* kres, float* scores,
-                         hipStream_t st) {
+                         const u16* k_mean_bf16, const float* kres, const float* bnorm,
+                         float* scores, hipStream_t st) {
   // A launch with at most 128 (kv head, query block) rows (small chunks)
   // splits each row's key tiles over floor(256 / rows) workgroups (at most
   // 16), so that every CU has work; whole prompts never split.
@@ -449,6 +497,7 @@ hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, cons
   a.q_scale = q_scale;
   a.kmean16 = k_mean_bf16;
   a.kres = kres;
+  a.bnorm = bnorm;
   a.scores = scores;
   a.errb = scores + g.num_rows * (int64_t)g.max_blocks;
   a.num_blocks = g.num_blocks;

@@ -69,30 +69,43 @@ def test_bound_is_reached_by_an_aligned_query():
     assert shift >= 0.95 * cs
 
 
-def _stats_fp32(acc, csc):
+def _stats_fp32(acc, csc, ref=None):
     """The scores kernel's fp32 statistics of one key column, step by step.
     acc [passes, 8 waves, 2 lanes, 32]: fp32 dot products of the column with
     the rows of a query block (a pass covers 512 rows: 8 waves x 2 chunks of
     32 rows; the lane pair l, l^32 of a wave holds 32 rows each); csc is the
-    log2-domain logit scale.  Per lane the scaled max, per wave the pair max
-    and the lanes' sequential exp2-sums (fma rounded once) added; per pass the
-    waves merged against the column max, L = (m + log2 sum) ln 2; passes
-    merged by a log-sum-exp.  float32 throughout."""
+    log2-domain logit scale; ref [passes] the column's log2-domain reference
+    per pass (None: the column max).  Per wave the lanes' sequential
+    exp2-sums against the reference (fma rounded once), added; a wave whose
+    sum is below 2^-64 falls back to its own max (per lane the scaled max,
+    pair max).  Per pass the waves merged against the largest of their
+    references, L = (m + log2 sum) ln 2; passes merged by a log-sum-exp.
+    float32 throughout."""
     f = np.float32
     ln2 = f(np.log(2.0))
     L = None
-    for pa in acc.astype(np.float32):
-        m_w = np.array([max(f(float(pa[w, k].max()) * float(csc)) for k in range(2))
-                        for w in range(pa.shape[0])], dtype=f)
+
+    def wave_sum(pw, r):
+        tot = f(0)
+        for k in range(2):
+            lane = f(0)
+            for v in pw[k]:
+                lane = f(lane + np.exp2(f(float(v) * float(csc) - float(r))))
+            tot = f(tot + lane)
+        return tot
+
+    for p, pa in enumerate(acc.astype(np.float32)):
+        m_w = np.zeros(pa.shape[0], dtype=f)
         s_w = np.zeros(pa.shape[0], dtype=f)
         for w in range(pa.shape[0]):
-            tot = f(0)
-            for k in range(2):
-                lane = f(0)
-                for v in pa[w, k]:
-                    lane = f(lane + np.exp2(f(float(v) * float(csc) - float(m_w[w]))))
-                tot = f(tot + lane)
-            s_w[w] = tot
+            s = None
+            if ref is not None:
+                m_w[w] = f(ref[p])
+                s = wave_sum(pa[w], m_w[w])
+            if s is None or not s >= 2.0 ** -64:
+                m_w[w] = max(f(float(pa[w, k].max()) * float(csc)) for k in range(2))
+                s = wave_sum(pa[w], m_w[w])
+            s_w[w] = s
         m = m_w.max()
         ssum = f(0)
         for w in range(pa.shape[0]):
@@ -107,12 +120,16 @@ def _stats_fp32(acc, csc):
 
 
 @pytest.mark.parametrize("mag", [1.0, 30.0, 1e3, 1e4])
-def test_fp32_statistics_within_the_selection_allowance(mag):
+@pytest.mark.parametrize("gap", [None, 0.0, 20.0, 60.0, 75.0])
+def test_fp32_statistics_within_the_selection_allowance(mag, gap):
     """The selection allows stat(L) = 1e-3 + 2^-17 |L| for the fp32
     statistics of a score (natural-log units); the emulated fp32 statistics
     stay below 1e-4 + 2^-19 |L| (the figure the interface states) at logit
-    magnitudes from 1 to 1e4, i.e. well inside the allowance."""
-    rng = np.random.default_rng(int(mag))
+    magnitudes from 1 to 1e4, i.e. well inside the allowance, whether the sums
+    run against the column max (gap None) or against a reference that many
+    log2 units above it (75: every wave's sum underflows the 2^-64 floor and
+    falls back to its max)."""
+    rng = np.random.default_rng(int(mag) + (0 if gap is None else 7 + int(gap)))
     scale = 1.0 / np.sqrt(128)
     csc = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
     for _ in range(4):
@@ -123,7 +140,10 @@ def test_fp32_statistics_within_the_selection_allowance(mag):
         exact_x = acc.astype(np.float64) * scale  # natural-log logits of the fp32 dot products
         M = exact_x.max()
         L64 = M + np.log(np.exp(exact_x - M).sum())
-        L32 = _stats_fp32(acc, csc)
+        ref = None
+        if gap is not None:
+            ref = [np.float32(float(pa.max()) * float(csc) + gap) for pa in acc]
+        L32 = _stats_fp32(acc, csc, ref)
         err = abs(L32 - L64)
-        assert err <= 1e-4 + 2.0 ** -19 * abs(L64), (mag, err)
+        assert err <= 1e-4 + 2.0 ** -19 * abs(L64), (mag, gap, err)
         assert err <= (1e-3 + 2.0 ** -17 * abs(L64)) / 4
