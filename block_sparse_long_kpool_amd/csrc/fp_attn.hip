@@ -153,6 +153,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int h = (int)(row_ord % a.lists);  // list owner (CSR row h * NQ + gq)
   const int gq = (int)(a.num_qblocks - 1 - row_ord / a.lists);
   const int64_t row = (int64_t)h * a.num_qblocks + gq;
+  // wave-uniform by construction; said explicitly so that the list bounds
+  // below become scalar loads
+  const int32_t* row_bounds = a.row_ptr + (int64_t)__builtin_amdgcn_readfirstlane((int)row);
   const int kvh = h / a.kvdiv;  // KV head of the owner's keys, values and pooled blocks
   const QBlock qb = uniform_block(query_block(a.m, gq));
   const int s = qb.s;
@@ -161,9 +164,17 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int nI = qb.nI;
   const int64_t tok0 = qb.tok0;
   const int64_t pooled_base = (int64_t)kvh * a.num_blocks + qb.kb0;
-  const int kbeg = DENSE ? 0 : a.row_ptr[row];
+  // The row's list is the head of a chain of dependent loads (list -> page
+  // table -> K/V gather), so it is read before anything else: its bounds by
+  // scalar loads, the first NT entries into registers ahead of the Q loads
+  // (a wait for them then does not wait for Q).
+  const int kbeg = DENSE ? 0 : load_uniform(row_bounds);
   // a valid list holds at most I + 1 blocks (the LDS tile list is sized for it)
-  const int nkept = DENSE ? I + 1 : min(max(a.row_ptr[row + 1] - kbeg, 0), I + 1);
+  const int nkept = DENSE ? I + 1 : min(max(load_uniform(row_bounds + 1) - kbeg, 0), I + 1);
+  // entry min(tid, nkept - 1); an empty list reads its own bound instead
+  // (branch-free, so that nothing waits for this load before the Q loads)
+  const int first_entry =
+      DENSE ? 0 : *(nkept > 0 ? a.col_idx + kbeg + min(tid, nkept - 1) : row_bounds);
   const int64_t ptrow = (int64_t)s * a.max_pages;
 
   const int hh = 2 * pack + (wave * RC) / 4;
@@ -172,7 +183,11 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int tbase = 32 * ((wave * RC) % 4);
 
   // ---- Q^T fragments (B operand), kept for the whole kernel ----
-  // (issued first: their latency overlaps the list set-up below)
+  // (issued right after the list: their latency overlaps the list set-up
+  // below).  Every lane loads unconditionally, rows past the block re-reading
+  // its last token, and invalid rows are zeroed afterwards: without a branch
+  // around the loads, a wait for the list loads issued before them does not
+  // have to wait for these.
   // lane owns row col of chunk rc; head-dim slots 64*half + 8*kk + i
   bf16x8 qf[RC][8];
   i32x8 qf8[RC][2];
@@ -182,36 +197,31 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     const int t0 = tbase + 32 * rc;
     nvalid[rc] = __builtin_amdgcn_readfirstlane(head_ok ? max(0, min(32, nI - t0)) : 0);  // wave-uniform
     const bool rvalid = col < nvalid[rc];
-    const int64_t e0 = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim + 64 * half;
+    const int64_t e0 = ((tok0 + min(t0 + col, nI - 1)) * a.hq + hq_idx) * (int64_t)kHeadDim + 64 * half;
     if constexpr (kFp8) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        i32x8 v = i32x8{};
-        if (rvalid) {
-          const i32x4* p = reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(a.q) + e0 + 32 * k2);
-          const i32x4 lo = p[0], hi = p[1];
-          v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        qf8[rc][k2] = v;
+        const i32x4* p = reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(a.q) + e0 + 32 * k2);
+        const i32x4 lo = p[0], hi = p[1];
+        const i32x8 v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        qf8[rc][k2] = rvalid ? v : i32x8{};
       }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) qf[rc][kk] = bf16x8{};
     } else if constexpr (QDT == FP_BF16) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        qf[rc][kk] = rvalid ? *reinterpret_cast<const bf16x8*>(reinterpret_cast<const u16*>(a.q) + e0 + 8 * kk)
-                            : bf16x8{};
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const u16*>(a.q) + e0 + 8 * kk);
+        qf[rc][kk] = rvalid ? v : bf16x8{};
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        if (rvalid) {
-          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + e0 + 8 * kk);
-          const float4 x = p[0], y = p[1];
-          qf[rc][kk] = bf16x8{f32_to_bf16(x.x), f32_to_bf16(x.y), f32_to_bf16(x.z), f32_to_bf16(x.w),
-                              f32_to_bf16(y.x), f32_to_bf16(y.y), f32_to_bf16(y.z), f32_to_bf16(y.w)};
-        } else {
-          qf[rc][kk] = bf16x8{};
-        }
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + e0 + 8 * kk);
+        const float4 x = p[0], y = p[1];
+        const bf16x8 v = bf16x8{f32_to_bf16(x.x), f32_to_bf16(x.y), f32_to_bf16(x.z), f32_to_bf16(x.w),
+                                f32_to_bf16(y.x), f32_to_bf16(y.y), f32_to_bf16(y.z), f32_to_bf16(y.w)};
+        qf[rc][kk] = rvalid ? v : bf16x8{};
       }
     }
   }
@@ -223,46 +233,19 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int nwords = (I >> 5) + 1;
   if (!DENSE && a.correction)
     for (int w = tid; w < nwords; w += NT) sm.kept_bits[w] = 0u;
-  if (!DENSE)
-    for (int i = tid; i < nkept; i += NT) sm.tiles[i] = (uint16_t)min(max(a.col_idx[kbeg + i], 0), I);
-  __syncthreads();
-  if (!DENSE && a.correction) {
-    for (int i = tid; i < nkept; i += NT) {
-      const int J = sm.tiles[i];
-      atomicOr(&sm.kept_bits[J >> 5], 1u << (J & 31));
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int ntile_p = (I >> 7) + 1;
-      int cnt = 0;
-      for (int base = 0; base < ntile_p; base += 64) {
-        const int pt = base + lane;
-        bool any_pruned = false;
-        if (pt < ntile_p) {
-          const int lo = pt * kBlock, hi = min(pt * kBlock + kBlock - 1, I);
-          for (int w = lo >> 5; w <= (hi >> 5); ++w) {
-            uint32_t m = ~sm.kept_bits[w];
-            const int wlo = w * 32;
-            if (wlo < lo) m &= ~((1u << (lo - wlo)) - 1u);
-            if (wlo + 31 > hi) m &= (hi - wlo >= 31) ? 0xFFFFFFFFu : ((1u << (hi - wlo + 1)) - 1u);
-            any_pruned |= m != 0u;
-          }
-        }
-        const unsigned long long mb = __ballot(any_pruned);
-        if (any_pruned) sm.tiles[nkept + cnt + __popcll(mb & ((1ull << lane) - 1ull))] = (uint16_t)pt;
-        cnt += __popcll(mb);
-      }
-      if (lane == 0) sm.npooled = cnt;
-    }
-    __syncthreads();
+  if (!DENSE) {
+    if (tid < nkept) sm.tiles[tid] = (uint16_t)min(max(first_entry, 0), I);
+    for (int i = tid + NT; i < nkept; i += NT) sm.tiles[i] = (uint16_t)min(max(a.col_idx[kbeg + i], 0), I);
   }
-  // wave-uniform counts: keep them in scalar registers
-  const int npooled = (!DENSE && a.correction) ? __builtin_amdgcn_readfirstlane(sm.npooled) : 0;
-  const int ntiles = nkept + npooled;
-  // KV split: this workgroup takes tiles [tbeg, tend) of the row's list
-  // (contiguous parts balanced by tile count; all of it without a split)
-  const int tbeg = (int)(((int64_t)split * ntiles) / a.splits);
-  const int tend = (int)(((int64_t)(split + 1) * ntiles) / a.splits);
+  __syncthreads();
+
+  // Tile range of this workgroup.  Without a KV split it is the whole list
+  // (kept tiles first): the first tile is then known before the pooled tiles
+  // are counted, and its page lookups and gathers are issued here, ahead of
+  // the bitmap and the scan below (tend is provisional until the scan).
+  const bool early = a.splits == 1 && nkept > 0;
+  int tbeg = 0;
+  int tend = nkept;
 
   // ---- tile staging -------------------------------------------------------
   // Kept block J: token rows J*128 .. +127 of the sequence (rows past the end
@@ -294,6 +277,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     const int p = p0 < len ? p0 : J * kBlock;
     const int cslot = page * psz + (small_pages ? (p & (psz - 1)) : (p % psz));
     sm.slot[sbuf][tid] = ((int64_t)cslot * a.hkv + kvh) * kHeadDim;
+  };
+  // slots of the first two tiles of the range (both page lookups in flight
+  // together), published by the caller's next barrier
+  auto prologue_slots = [&]() {
+    const int page0 = fetch_page(tbeg);
+    const int page1 = fetch_page(tbeg + 1);
+    publish_slot(tbeg, page0, tbeg & 1);
+    publish_slot(tbeg + 1, page1, (tbeg + 1) & 1);
   };
   auto issue_tile = [&](int t, int buf) {
     const bool pooled = t >= nkept;
@@ -378,6 +369,50 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     }
   };
 
+  if (early) {
+    prologue_slots();
+    __syncthreads();
+    issue_tile(0, 0);  // a kept tile: needs neither the bitmap nor the pooled list
+  }
+
+  if (!DENSE && a.correction) {
+    for (int i = tid; i < nkept; i += NT) {
+      const int J = sm.tiles[i];
+      atomicOr(&sm.kept_bits[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int ntile_p = (I >> 7) + 1;
+      int cnt = 0;
+      for (int base = 0; base < ntile_p; base += 64) {
+        const int pt = base + lane;
+        bool any_pruned = false;
+        if (pt < ntile_p) {
+          const int lo = pt * kBlock, hi = min(pt * kBlock + kBlock - 1, I);
+          for (int w = lo >> 5; w <= (hi >> 5); ++w) {
+            uint32_t m = ~sm.kept_bits[w];
+            const int wlo = w * 32;
+            if (wlo < lo) m &= ~((1u << (lo - wlo)) - 1u);
+            if (wlo + 31 > hi) m &= (hi - wlo >= 31) ? 0xFFFFFFFFu : ((1u << (hi - wlo + 1)) - 1u);
+            any_pruned |= m != 0u;
+          }
+        }
+        const unsigned long long mb = __ballot(any_pruned);
+        if (any_pruned) sm.tiles[nkept + cnt + __popcll(mb & ((1ull << lane) - 1ull))] = (uint16_t)pt;
+        cnt += __popcll(mb);
+      }
+      if (lane == 0) sm.npooled = cnt;
+    }
+    __syncthreads();
+  }
+  // wave-uniform counts: keep them in scalar registers
+  const int npooled = (!DENSE && a.correction) ? __builtin_amdgcn_readfirstlane(sm.npooled) : 0;
+  const int ntiles = nkept + npooled;
+  // KV split: this workgroup takes tiles [tbeg, tend) of the row's list
+  // (contiguous parts balanced by tile count; all of it without a split)
+  tbeg = (int)(((int64_t)split * ntiles) / a.splits);
+  tend = (int)(((int64_t)(split + 1) * ntiles) / a.splits);
+
   // log2-domain logit scales: kept tiles and pooled tiles
   float c_kept = a.softmax_scale * kLog2e;
   float c_pool = c_kept;
@@ -398,15 +433,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     for (int dc = 0; dc < 4; ++dc) o[rc][dc] = f32x16{};
   }
 
-  // prologue: slots of the first two tiles, gathers of the first
-  {
-    const int page0 = fetch_page(tbeg);  // both page lookups in flight together
-    const int page1 = fetch_page(tbeg + 1);
-    publish_slot(tbeg, page0, tbeg & 1);
-    publish_slot(tbeg + 1, page1, (tbeg + 1) & 1);
+  // prologue: slots of the first two tiles, gathers of the first (already in
+  // flight on the early path)
+  if (!early) {
+    prologue_slots();
+    __syncthreads();
+    if (tbeg < tend) issue_tile(tbeg, tbeg & 1);
   }
-  __syncthreads();
-  if (tbeg < tend) issue_tile(tbeg, tbeg & 1);
   wait_vm();
   __syncthreads();
 

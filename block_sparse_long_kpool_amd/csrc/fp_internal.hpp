@@ -221,6 +221,14 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Read through the constant address space: with a wave-uniform address this
+// is a scalar load (tracked by lgkmcnt, so it does not wait behind vector
+// loads in flight).  Only for data that no thread writes during the kernel.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // LDS has 64 banks of 4 bytes (256 bytes per row of banks).  Physical 16-byte
 // chunk of logical chunk c in row r of a 256-byte bf16 row: c ^ g(r & 15),
 // g swapping the two 2-bit halves of the row index.  Then (a) 16 consecutive
