@@ -124,7 +124,7 @@ void dense_geometry(Geometry* g) {
 
 struct DiscoverWs { int32_t* kboff; int32_t* qboff; u16* km16; float* kres; float* bnorm; };
 struct SelectWs { int32_t* kboff; int32_t* qboff; uint32_t* bits; int32_t* counts; };
-struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; float* opart; float* lpart; };
+struct AttnWs { int32_t* kboff; int32_t* qboff; u16* km16; u16* vm16; float* opart; float* lpart; int* queue; };
 
 SeqMap seq_map(const fp_problem* p, int32_t* kboff, int32_t* qboff) {
   SeqMap m;
@@ -168,6 +168,7 @@ size_t ws_layout(const Geometry& g, int which, void* base, void* out) {
     w.qboff = (int32_t*)take(boff_bytes);
     w.km16 = (u16*)take(pooled16);
     w.vm16 = (u16*)take(pooled16);
+    w.queue = (int*)take(sizeof(int));  // item counter of the attention kernel
     w.opart = w.lpart = nullptr;
     const int splits = attn_splits(g);
     if (splits > 1) {  // partial outputs and lse of the KV-split parts
@@ -434,11 +435,11 @@ int fp_sparse_attn_paged(const fp_problem* p, const void* q, const void* k_cache
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const SeqMap m = seq_map(p, w.kboff, w.qboff);
   if ((st = hip_status(launch_attn_prep(g, m, mean_correction ? k_mean : nullptr, v_mean, w.km16,
-                                        w.vm16, s), "attn prep")))
+                                        w.vm16, w.queue, s), "attn prep")))
     return st;
   return hip_status(launch_attn(g, m, p->page_table_dev, q, k_cache, v_cache, p->q_scale_dev,
                                 p->k_scale_dev, row_ptr, col_idx, w.km16, w.vm16,
-                                mean_correction ? 1 : 0, out, lse, w.opart, w.lpart, s, false),
+                                mean_correction ? 1 : 0, out, lse, w.opart, w.lpart, w.queue, s, false),
                     "attn");
 }
 
@@ -456,11 +457,11 @@ int fp_dense_attn_paged(const fp_problem* p, const void* q, const void* k_cache,
   ws_layout(g, FP_WS_ATTN, ws, &w);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const SeqMap m = seq_map(p, w.kboff, w.qboff);
-  if ((st = hip_status(launch_attn_prep(g, m, nullptr, nullptr, w.km16, w.vm16, s), "attn prep")))
+  if ((st = hip_status(launch_attn_prep(g, m, nullptr, nullptr, w.km16, w.vm16, w.queue, s), "attn prep")))
     return st;
   return hip_status(launch_attn(g, m, p->page_table_dev, q, k_cache, v_cache, p->q_scale_dev,
                                 p->k_scale_dev, nullptr, nullptr, w.km16, w.vm16, 0, out, lse, w.opart,
-                                w.lpart, s, true),
+                                w.lpart, w.queue, s, true),
                     "dense attn");
 }
 

@@ -64,6 +64,11 @@ constexpr int kTileElems = kBlock * kHeadDim;  // one bf16 tile = 32 KiB
 // waves per workgroup: two waves per SIMD, 32 query rows each (a form with
 // four waves of 64 rows needs more than 512 registers per wave and spills)
 constexpr int kAttnWaves = 8;
+// On-demand tail of the item order (launches of at least kAttnDynMinItems
+// items): its share of the items and the extra workgroups, in percent of it.
+constexpr int64_t kAttnDynMinItems = 4096;
+constexpr int64_t kAttnDynFracPct = 15;
+constexpr int64_t kAttnDynSlackPct = 50;
 
 struct AttnArgs {
   SeqMap m;
@@ -82,6 +87,9 @@ struct AttnArgs {
   float* opart;  // splits > 1: [splits, T, Hq, d] partial outputs (each normalised by its own sum)
   float* lpart;  // splits > 1: [splits, Hq, T] partial lse (natural log; -inf for an empty part)
   int splits;    // workgroups per (row, head pack), each over a contiguous part of the tile list
+  int nitems;    // work items: rows (rounded up to 8) x packs x splits
+  int dyn_begin; // items from here on are handed out through *queue (see the kernel)
+  int* queue;    // counter of the dynamic items, zero at launch
   int64_t num_blocks;   // NK (pooled rows per KV head)
   int64_t num_qblocks;  // NQ (CSR rows per list owner)
   int64_t total_tokens;
@@ -103,6 +111,7 @@ struct SharedMem {
   // tile list of the row: kept blocks (list order), then pooled tile indices
   uint16_t tiles[kMaxBlocksPerSeq + kMaxBlocksPerSeq / kBlock];
   int npooled;
+  int item;  // a dynamic workgroup's item (-1: none left)
 };
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const u16* p) {
@@ -142,7 +151,23 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int col = lane & 31;
 
   // ---- work item: XCD-grouped (row, pack), heaviest rows first ----
-  const int b = blockIdx.x;
+  // Workgroups are dispatched to the eight XCDs in turn, so workgroup b runs
+  // on XCD b % 8 and item b with it: the packs of a row (items 8 apart) run
+  // together on one XCD and share its L2.  The XCDs do not all run at the
+  // same speed, though, so the last items (dyn_begin on) are handed out on
+  // demand instead: the workgroups from dyn_begin on (the grid has some
+  // beyond nitems) take the next one from a counter, and a workgroup that
+  // finds none left exits.  XCDs that are ahead thus take more of them.
+  int b = blockIdx.x;
+  if (b >= a.dyn_begin) {
+    if (tid == 0) {
+      const int j = atomicAdd(a.queue, 1);
+      sm.item = j < a.nitems - a.dyn_begin ? a.dyn_begin + j : -1;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(sm.item);
+    if (b < 0) return;
+  }
   const int xcd = b & 7;
   const int kq = b >> 3;
   const int pack = kq % a.packs;
@@ -839,12 +864,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   if (lse && lane == 0) lse[(int64_t)hh * T + tok] = m + logf(tot);
 }
 
-// Block offsets of the map (last block of the grid) and bf16 copies of the
-// pooled keys / values (each rounded once from float64).
+// Block offsets of the map and the attention's item counter (last block of
+// the grid) and bf16 copies of the pooled keys / values (each rounded once
+// from float64).
 __global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const double* __restrict__ km,
                                                         const double* __restrict__ vm, u16* __restrict__ km16,
-                                                        u16* __restrict__ vm16, int64_t n) {
+                                                        u16* __restrict__ vm16, int64_t n, int* __restrict__ queue) {
   if (blockIdx.x == gridDim.x - 1) {
+    if (threadIdx.x == 0) *queue = 0;  // the attention kernel's item counter
     plan_offsets(m);
     return;
   }
@@ -865,11 +892,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(SeqMap m, const double* 
 }  // namespace
 
 hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const double* k_mean,
-                            const double* v_mean, u16* km16, u16* vm16, hipStream_t st) {
+                            const double* v_mean, u16* km16, u16* vm16, int* queue, hipStream_t st) {
   const int64_t n = (int64_t)g.hkv * g.num_blocks * kHeadDim;
   const unsigned conv = k_mean ? (unsigned)((n / 4 + 255) / 256) : 0u;
   hipLaunchKernelGGL(attn_prep_kernel, dim3(conv + 1), dim3(256), 0, st, m, k_mean, v_mean, km16,
-                     vm16, n);
+                     vm16, n, queue);
   return hipGetLastError();
 }
 
@@ -884,7 +911,7 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
                        const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                        const u16* km16, const u16* vm16, int correction, void* out, float* lse,
-                       float* opart, float* lpart, hipStream_t st, bool dense) {
+                       float* opart, float* lpart, int* queue, hipStream_t st, bool dense) {
   AttnArgs a;
   a.m = m;
   a.page_table = page_table;
@@ -917,7 +944,20 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
   a.correction = dense ? 0 : correction;
   a.softmax_scale = g.softmax_scale;
   const int64_t rows = (int64_t)g.lists * g.num_qblocks;
-  const unsigned grid = (unsigned)(((rows + 7) / 8) * 8 * a.packs * a.splits);
+  const int64_t nitems = ((rows + 7) / 8) * 8 * a.packs * a.splits;
+  if (nitems > INT32_MAX / 2) return hipErrorInvalidValue;
+  // Launches of many waves per CU hand their last kAttnDynFrac items out on
+  // demand, with kAttnDynSlack of that count in extra workgroups; small
+  // launches keep the static order.
+  int64_t ndyn = 0, slack = 0;
+  if (nitems >= kAttnDynMinItems) {
+    ndyn = nitems * kAttnDynFracPct / 100;
+    slack = ndyn * kAttnDynSlackPct / 100;
+  }
+  a.nitems = (int)nitems;
+  a.dyn_begin = (int)(nitems - ndyn);
+  a.queue = queue;
+  const unsigned grid = (unsigned)(nitems + slack);
   const size_t shm = sizeof(SharedMem);
 #define FP_ATTN_D(QD, VD, OD, DN)                                                              \
   do {                                                                                         \

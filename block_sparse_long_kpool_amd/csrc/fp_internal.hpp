@@ -318,7 +318,7 @@ hipError_t launch_select_ranked(const Geometry& g, const SeqMap& m, const float*
 
 // Block offsets of the map plus bf16 copies of the pooled keys / values.
 hipError_t launch_attn_prep(const Geometry& g, const SeqMap& m, const double* k_mean,
-                            const double* v_mean, u16* km16, u16* vm16, hipStream_t st);
+                            const double* v_mean, u16* km16, u16* vm16, int* queue, hipStream_t st);
 
 // Parts per row of the attention launch (1: no split).
 int attn_splits(const Geometry& g);
@@ -329,6 +329,7 @@ hipError_t launch_attn(const Geometry& g, const SeqMap& m, const int32_t* page_t
                        const void* k_cache, const void* v_cache, const float* q_scale,
                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                        const u16* km16, const u16* vm16, int correction, void* out, float* lse,
-                       float* opart, float* lpart, hipStream_t st, bool dense);
+                       float* opart, float* lpart, int* queue, hipStream_t st,
+                       bool dense);
 
 }  // namespace fp
