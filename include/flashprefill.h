@@ -149,6 +149,9 @@ int64_t fp_scores_elems(const fp_problem* p);     /* Lo * NQ * (n_max + 1): the
 int64_t fp_csr_capacity(const fp_problem* p);     /* Lo * sum over query blocks of
                                                      (I + 1): every causal block kept
                                                      (<= INT32_MAX)               */
+/* Bytes of the workspace of kind `which` (fp_workspace_kind).  A workspace
+ * holds intermediate data and counters of one call: calls that may run at the
+ * same time (different streams) need workspaces of their own. */
 size_t fp_workspace_bytes(const fp_problem* p, int32_t which);
 const char* fp_status_string(int32_t status);
 const char* fp_last_error(void);
