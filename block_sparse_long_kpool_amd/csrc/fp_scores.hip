@@ -352,16 +352,8 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
     }
   };
 
-  // Largest residual bound of the row's key blocks (published by the first
-  // barrier of the pass loop).
-  {
-    const float* kres = a.kres + (int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0;
-    float dm = 0.f;
-    for (int J = (int)threadIdx.x; J < ncols; J += 64 * kWaves) dm = fmaxf(dm, kres[J]);
-    dm = wave_max(dm);
-    if (lane == 0) sm.red[0][wave] = dm;
-  }
   float qn2 = 0.f;  // largest squared query-row norm (q_scale included), all passes
+
 
   for (int pass = 0; pass * kChunksPerPass < nchunks; ++pass) {
     // ---- Q fragments of this pass (read once) ----
@@ -384,6 +376,17 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       qsf[rc] = QDT == FP_E4M3 ? a.q_scale[hq_idx] : 1.f;
       csc[rc] = a.logit_scale * kLog2e * qsf[rc];
     }
+    // the first key tile does not depend on Q: in flight together with it
+    stage(tile0, tile0 & 1);
+    if (pass == 0) {
+      // largest residual bound of the row's key blocks (published by the
+      // barrier below), its loads in flight with the Q loads
+      const float* kres = a.kres + (int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0;
+      float dm = 0.f;
+      for (int J = (int)threadIdx.x; J < ncols; J += 64 * kWaves) dm = fmaxf(dm, kres[J]);
+      dm = wave_max(dm);
+      if (lane == 0) sm.red[0][wave] = dm;
+    }
     {
       // squared norms of this wave's rows (lanes l and l^32 hold the halves)
       float wn = 0.f;
@@ -404,7 +407,6 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       if (lane == 0) sm.red[1][wave] = wn;
     }
 
-    stage(tile0, tile0 & 1);
     wait_vm();
     __syncthreads();
     float qp2 = 0.f;  // largest squared query-row norm of this pass
