@@ -200,6 +200,48 @@ def compare_lists_all_rows(prob, scores, rp, ci, alpha, sinks=256, local=512):
     return len(scores), band, mism
 
 
+def check_ranked_row(mode, param, I, got, L_fast, L_exact, err, sinks=256, local=512, B=128):
+    """One row of a ranked selection (top-k / top-p with parameter param)
+    made from the fast scores L_fast, against the exact scores L_exact: a
+    decision may differ from the exact selection only between blocks whose
+    exact scores are within their error bounds err (array over J <= I) of
+    each other, and for top-p the exact mass share of the prefix taken stays
+    within the ratio those errors allow.  Returns the number of decisions
+    that differ from the exact selection; raises AssertionError otherwise."""
+    from oracle import forced_blocks, rank_order, select_row_topk, select_row_topp
+    Lx = np.asarray(L_exact, dtype=np.float64)[:I + 1]
+    forced = forced_blocks(I, sinks, local, B)
+    if mode == "topk":
+        ndiff = len(got ^ set(select_row_topk(Lx, I, param, sinks, local, B).tolist()))
+    else:
+        if param <= 0:
+            assert got == set(np.nonzero(forced)[0].tolist()), ("forced only", I)
+            return 0
+        ndiff = len(got ^ set(select_row_topp(Lx, I, param, sinks, local, B).tolist()))
+        # the prefix of the fast ranking ends between the last kept
+        # non-forced block and the end of the kept run (forced blocks are kept
+        # wherever they rank); some end in that range must meet the top-p
+        # condition under the exact scores, up to the slack
+        order = rank_order(np.asarray(L_fast, dtype=np.float64)[:I + 1], I)
+        m_max = int(np.cumprod([J in got for J in order]).sum()) - 1
+        m_min = max([i for i, J in enumerate(order) if J in got and not forced[J]] + [0])
+        wx = np.exp(Lx - Lx.max())
+        share = np.cumsum(wx[order]) / wx.sum()
+        slack = float(np.expm1(2 * float(np.max(err)))) + 1e-4
+        ok = [m for m in range(m_min, m_max + 1)
+              if share[m] >= param * (1 - slack) and (m == 0 or share[m - 1] < param * (1 + slack))]
+        assert ok, ("top-p mass", I, m_min, m_max, share[m_min:m_max + 1])
+    # every kept non-forced block ranks no lower than any dropped one, up to
+    # the bounds
+    ins = [J for J in got if not forced[J]]
+    outs = [J for J in range(I + 1) if J not in got]
+    if ins and outs:
+        lo = min(Lx[J] + err[J] for J in ins)
+        hi = max(Lx[J] - err[J] for J in outs)
+        assert lo >= hi, ("ranking", I, lo, hi)
+    return ndiff
+
+
 def sample_rows(w, n_per_head, seed=0, head_lists=False):
     """Seeded sample of (owner, s, I) rows, always including each sequence's
     first and last query block."""
