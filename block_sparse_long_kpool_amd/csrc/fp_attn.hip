@@ -11,9 +11,10 @@
 // gfx950 design:
 //   * workgroup = 256 query rows = 2 heads of one GQA group x the 128 tokens
 //     of one query block, split over 8 waves (two per SIMD, one 32-row chunk
-//     each).  The g/2
-//     workgroups of a group get consecutive ids on the same XCD so their K/V
-//     reads share that L2.
+//     each).  The g/2 workgroups of a group get ids 8 apart, i.e. the same
+//     XCD at about the same time, so their K/V reads share that L2; the last
+//     15 % of the items are handed out on demand so that the XCDs finish
+//     together.
 //   * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no staging
 //     registers): every lane gathers 16 bytes of a token row through the page
 //     table and the hardware writes lane i's bytes at LDS base + 16 i.  Rows
