@@ -12,7 +12,10 @@ from gpu_parity_util import log
 pytestmark = pytest.mark.gpu
 
 
-def _spec(seed, qk="bf16"):
+def _spec(seed, qk="bf16", size="small"):
+    if size == "32k":  # 4096 attention items: the on-demand tail of the item order is active
+        return custom_spec(name=f"graph{seed}", seqlens=(32768,), num_q_heads=32, num_kv_heads=4,
+                           page_size=64, qk_dtype=qk, seed=seed)
     return custom_spec(name=f"graph{seed}", seqlens=(700, 300, 129), num_q_heads=8,
                        num_kv_heads=2, page_size=32, qk_dtype=qk, seed=seed)
 
@@ -23,12 +26,12 @@ def _snapshot(pipe):
                 scores=pipe.scores.cpu().numpy(), k_mean=pipe.k_mean.cpu().numpy())
 
 
-@pytest.mark.parametrize("qk", ["bf16", "e4m3"])
-def test_graph_replays_match_eager(qk):
+@pytest.mark.parametrize("qk,size", [("bf16", "small"), ("e4m3", "small"), ("bf16", "32k")])
+def test_graph_replays_match_eager(qk, size):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
-    log(f"case graph {qk}")
-    ws = [make_workload(_spec(s, qk)) for s in (160, 161)]
+    log(f"case graph {qk} {size}")
+    ws = [make_workload(_spec(s, qk, size)) for s in (160, 161)]
     refs = []
     for w in ws:
         p = Pipeline(upload(w, "cuda"))
