@@ -406,10 +406,14 @@ def test_per_query_head_lists_parity(name, kw, ctx, splits):
 
 
 def test_per_query_head_lists_gqa_32k_sampled():
-    """32K prompt, Hq=32 / Hkv=4, per-query-head lists on sampled rows."""
+    """32K prompt, Hq=32 / Hkv=4, per-query-head lists: every one of the
+    8192 rows' lists against the oracle's selection from its float64
+    per-head scores, scores and outputs on sampled rows."""
     log("case gqa_32k head_lists")
     w = make_workload(spec_for("gqa_32k"))
     g = run_gpu(w, 0.1, head_lists=True)
+    prob, sc = oracle_scores_all_rows(w, head_lists=True)
+    compare_lists_all_rows(prob, sc, g["row_ptr"], g["col_idx"], 0.1)
     compare(w, g, 0.1, rows=sample_rows(w, 2, head_lists=True), check_pool=False,
             head_lists=True)
 
