@@ -350,7 +350,7 @@ def main():
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the alpha sweep x correction (written to --sweep-out)")
-    ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
+    ap.add_argument("--sweep-out", default="sweep.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--select", default="threshold", metavar="MODE",
                     help="block selection: threshold (alpha), topk:K or topp:P (the ranked "
@@ -374,8 +374,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the op shards by KV head with no exchange; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the op would shard by KV head with no exchange).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1,4 +1,4 @@
-"""Buffer-owning driver of the three library calls.
+"""Buffer-owning wrapper of the three library calls.
 
 `Pipeline` allocates (with torch, on the device) every buffer the three calls
 need for one batch shape, then runs discover -> select -> attention on the
