@@ -24,8 +24,7 @@ bf16 bit patterns and e4m3 codes are decoded exactly (e4m3 code x fp32 scale
 formed in fp64); fp32 inputs are rounded to bf16 first (the library ingests
 fp32 by rounding to bf16, nearest-even).
 
-Readings taken where the pages leave a step open (each also listed in the
-design notes):
+Readings taken where the pages leave a step open:
   R1 pooling statistic is the mean ([V1] 3.1 key pooling; [V2] 4.1 uses the
      block key mean); n_J = number of tokens actually in block J.
   R2 discovery score: rows(I) = every (query head of the KV group, token of
