@@ -238,6 +238,16 @@ def test_chunked_prefill_128k_last_16k():
     compare(wc, gc, 0.1, rows=sample_rows(wc, 4), check_pool=False)
 
 
+def test_chunked_prefill_varlen_last_8k():
+    """The varlen e4m3 batch (16-token pages, round-robin) with the last 8K
+    tokens of every sequence as one chunk each (the 8K sequence entirely):
+    bit-identical to the whole batch's rows."""
+    log("case chunk_varlen_last8k")
+    w = make_workload(spec_for("varlen_4x"))
+    lens = np.diff(np.asarray(w.cu_seqlens))
+    _chunk_vs_whole(w, tuple(int(n) - 8192 for n in lens))
+
+
 @pytest.mark.parametrize("splits", [2, 3, 8])
 def test_forced_kv_split_gqa_32k(splits):
     """32K prompt with every row forced into 2, 3 or 8 parts (parts may be
