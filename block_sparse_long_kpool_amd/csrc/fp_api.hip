@@ -271,8 +271,10 @@ int fp_discover(const fp_problem* p, const void* q, const void* k_cache, const v
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const SeqMap m = seq_map(p, w.kboff, w.qboff);
   if ((st = hip_status(launch_plan(m, s), "plan"))) return st;
+  // the discovery copy of the key means is pre-scaled to log2-domain logits
+  const double lscale = g.softmax_scale_d * 1.4426950408889634074;  // log2(e)
   if ((st = hip_status(launch_pool(g, m, p->page_table_dev, k_cache, v_cache, p->k_scale_dev,
-                                   k_mean, v_mean, w.km16, w.kres, w.bnorm, s), "pool")))
+                                   lscale, k_mean, v_mean, w.km16, w.kres, w.bnorm, s), "pool")))
     return st;
   return hip_status(launch_scores(g, m, q, p->q_scale_dev, w.km16, w.kres, w.bnorm, block_scores, s),
                     "scores");

@@ -296,8 +296,8 @@ hipError_t launch_plan(const SeqMap& m, hipStream_t st);
 // accumulation of 128 exact products).
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
-                       double* k_mean, double* v_mean, u16* k_mean_bf16, float* kres,
-                       float* bnorm, hipStream_t st);
+                       double lscale, double* k_mean, double* v_mean, u16* k_mean_bf16,
+                       float* kres, float* bnorm, hipStream_t st);
 
 // Scores [lists * NQ, max_blocks] followed by one error bound per score row.
 // bnorm: |bf16(kbar_J)|_2 per pooled key (rounded up), from the pooling pass.

@@ -46,13 +46,16 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) 
 // values of a block (bf16 or e4m3 codes, 8 and 4 significant bits) add up
 // exactly unless their magnitudes span more than ~2^38, and the division by
 // n_J rounds once, so the means are the exact block means to float64
-// rounding.  Summation order is fixed (deterministic).
+// rounding.  Summation order is fixed (deterministic).  The discovery copy
+// of each key mean is kbar_J * lscale (lscale = softmax_scale * log2(e)),
+// rounded once to bf16: dot products with it are log2-domain logits.
 template <int KDT, int VDT>
 __global__ __launch_bounds__(256) void pool_kernel(
     SeqMap m, const int32_t* __restrict__ page_table, int max_pages, int page_size, int hkv,
     int64_t num_blocks, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
-    const float* __restrict__ k_scale, double* __restrict__ k_mean, double* __restrict__ v_mean,
-    u16* __restrict__ k_mean_bf16, float* __restrict__ kres, float* __restrict__ bnorm) {
+    const float* __restrict__ k_scale, double lscale, double* __restrict__ k_mean,
+    double* __restrict__ v_mean, u16* __restrict__ k_mean_bf16, float* __restrict__ kres,
+    float* __restrict__ bnorm) {
   __shared__ double red[16][kHeadDim + 2];
   __shared__ double2 nred[kHeadDim / 64];
   const int gb = blockIdx.x;
@@ -116,14 +119,15 @@ __global__ __launch_bounds__(256) void pool_kernel(
       v_mean[o] = mean;
     } else {
       k_mean[o] = mean;
-      // kbar rounded to bf16 (once, from the float64 mean) for the
+      // lscale * kbar rounded to bf16 (once, from float64) for the
       // discovery MFMA, and the squared norms of its rounding residual
       // (exact: the residual of a nearest rounding is representable) and
       // of the rounded value, summed over the 128 dims (two waves)
-      const u16 hb = f64_to_bf16_bits(mean);
+      const double ms = mean * lscale;
+      const u16 hb = f64_to_bf16_bits(ms);
       k_mean_bf16[o] = hb;
       const double hv = (double)bf16_bits_to_f32(hb);
-      const double r = mean - hv;
+      const double r = ms - hv;
       const double r2 = wave_sum_d(r * r), h2 = wave_sum_d(hv * hv);
       if ((d & 63) == 0) nred[d >> 6] = make_double2(r2, h2);
     }
@@ -132,9 +136,10 @@ __global__ __launch_bounds__(256) void pool_kernel(
     __syncthreads();
     if (threadIdx.x == 0) {
       const double r2 = nred[0].x + nred[1].x, h2 = nred[0].y + nred[1].y;
-      // |kbar_J - bf16(kbar_J)|_2 + kAccumRel |bf16(kbar_J)|_2, rounded up
-      // to fp32 (the factor covers the float64 sums, square roots and the
-      // final rounding)
+      // |s_J - bf16(s_J)|_2 + kAccumRel |bf16(s_J)|_2 with s_J = lscale *
+      // kbar_J, rounded up to fp32 (the factor covers the float64 sums,
+      // square roots and the final rounding; kAccumRel, twice the fp32
+      // accumulation term, also covers the float64 rounding of the scaling)
       const double b = (sqrt(r2) + kAccumRel * sqrt(h2)) * (1.0 + 0x1p-40);
       kres[(int64_t)h * num_blocks + gb] = (float)b * (1.f + 0x1p-22f);
       bnorm[(int64_t)h * num_blocks + gb] = (float)sqrt(h2) * (1.f + 0x1p-22f);
@@ -144,13 +149,13 @@ __global__ __launch_bounds__(256) void pool_kernel(
 
 hipError_t launch_pool(const Geometry& g, const SeqMap& m, const int32_t* page_table,
                        const void* k_cache, const void* v_cache, const float* k_scale,
-                       double* k_mean, double* v_mean, u16* k_mean_bf16, float* kres,
-                       float* bnorm, hipStream_t st) {
+                       double lscale, double* k_mean, double* v_mean, u16* k_mean_bf16,
+                       float* kres, float* bnorm, hipStream_t st) {
   dim3 grid((unsigned)g.num_blocks, (unsigned)g.hkv, 2);
 #define FP_POOL(KD, VD)                                                                       \
   hipLaunchKernelGGL((pool_kernel<KD, VD>), grid, dim3(256), 0, st, m, page_table,            \
                      g.max_pages, g.page_size, g.hkv, g.num_blocks, k_cache,                   \
-                     v_cache, k_scale, k_mean, v_mean, k_mean_bf16, kres, bnorm)
+                     v_cache, k_scale, lscale, k_mean, v_mean, k_mean_bf16, kres, bnorm)
   if (g.qk_dtype == FP_BF16 && g.v_dtype == FP_BF16) FP_POOL(FP_BF16, FP_BF16);
   else if (g.qk_dtype == FP_E4M3 && g.v_dtype == FP_BF16) FP_POOL(FP_E4M3, FP_BF16);
   else if (g.qk_dtype == FP_F32 && g.v_dtype == FP_F32) FP_POOL(FP_F32, FP_F32);

@@ -15,31 +15,36 @@
 //     in passes of 8 waves x 2 chunks x 32 rows, each wave holding the Q
 //     fragments of its two chunks in registers for the whole pass, so Q is
 //     read from HBM once (passes = g / 4).
-//   * pooled keys (kbar rounded to bf16, L2-resident) stream through
+//   * pooled keys s_J = bf16(softmax_scale log2(e) kbar_J) (scaled in float64
+//     and rounded once by the pooling pass, L2-resident) stream through
 //     double-buffered LDS in tiles of 128 keys, copied with
 //     global_load_lds_dwordx4 (no staging registers) into XOR-swizzled 256-B
 //     rows, so the MFMA operand reads are conflict-free.
-//   * X = Q . Kbar^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  In
-//     the result layout a lane owns one pooled-key column and 16 rows of each
-//     chunk: the exp-sum is lane-local, lanes l and l^32 are merged with one
-//     v_permlane32_swap, and the 8 waves through LDS once per tile.
-//   * no column max: the sums are taken against a per-column reference known
-//     before the MFMAs, softmax_scale * max_r |q_r|_2 * |bf16(kbar_J)|_2
-//     (Cauchy-Schwarz bounds every logit of the column by it), so
-//     S = sum_r exp(x_rJ - ref) <= R and L = ref + ln S; a column whose sum
-//     falls below 2^-64 (reference far above its logits) is recomputed with
-//     its true max, so the result keeps the same fp32 accuracy.
-//   * error bound instead of a second MFMA term: rounding kbar_J to bf16
-//     moves x_rJ by at most softmax_scale * |q_r|_2 * |kbar_J - bf16(kbar_J)|_2
-//     (Cauchy-Schwarz), and a log-sum-exp over rows moves by at most the
-//     largest such shift.  The kernel writes that bound per score row
-//     (largest query-row norm of the row times the largest residual bound of
-//     its key blocks, from the pooling pass); the selection re-evaluates in
-//     float64 every entry the bound cannot decide.
+//   * X = Q . S^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation: the
+//     log2-domain logits come straight out of the matrix core (e4m3 queries:
+//     times the head's q_scale).  In the result layout a lane owns one
+//     pooled-key column and 16 rows of each chunk: the exp-sum is lane-local,
+//     lanes l and l^32 are merged with one v_permlane32_swap, and the 8 waves
+//     through LDS once per tile.
+//   * no column max: max_r |q_r|_2 * |s_J|_2 bounds every logit of column J
+//     (Cauchy-Schwarz).  When that bound is at most kDirectMax for every
+//     column of the row (bf16 / fp32 queries), the exp2-sums run on the
+//     logits as they are, one exp and one add per element (no term can
+//     overflow); otherwise against the bound as a per-column reference,
+//     S = sum_r 2^(x_rJ - ref), L = ref + log2 S.  A wave whose sum for a
+//     column falls below 2^-64 recomputes that chunk against its true max,
+//     so the result keeps the same fp32 accuracy.
+//   * error bound instead of a second MFMA term: rounding s_J to bf16 moves
+//     x_rJ by at most |q_r|_2 * |lscale kbar_J - s_J|_2 (Cauchy-Schwarz), and
+//     a log-sum-exp over rows moves by at most the largest such shift.  The
+//     kernel writes that bound per score row (largest query-row norm of the
+//     row times the largest residual bound of its key blocks, from the
+//     pooling pass); the selection re-evaluates in float64 every entry the
+//     bound cannot decide.
 //   * software pipeline inside a wave: the MFMAs of key chunk j+1 (second
-//     accumulator set) are independent of the max / exp / sum of chunk j, so
-//     the matrix core and the VALU overlap; the logit scale is folded into one
-//     fma per element, and masking runs only for the ragged last block.
+//     accumulator set) are independent of the exp-sums of chunk j, so the
+//     matrix core and the VALU overlap; masking runs only for the ragged last
+//     block.
 #include <algorithm>
 
 #include "fp_internal.hpp"
@@ -54,14 +59,14 @@ constexpr int kChunksPerPass = kWaves * kRC;   // 512 rows per pass
 constexpr int kJT = 128;                       // pooled keys per LDS tile
 constexpr int kJC = kJT / 32;                  // 32-key chunks per tile
 constexpr int kTerm = kJT * kHeadDim;          // bf16 elements of one term of a tile
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct ScoresSmem {
   u16 kb[2][kTerm];              // [buffer]: 64 KiB
-  float bn[2][kJT];              // [buffer]: |bf16(kbar_J)|_2 of the tile's keys
+  float bn[2][kJT];              // [buffer]: |s_J|_2 of the tile's keys
   float2 part[2][kWaves][kJT];   // per wave (reference, sum) of each key, by buffer
-  float red[2][kWaves];          // per wave: largest residual bound, largest row norm^2
+  float red[3][kWaves];          // per wave: largest residual bound, largest row norm^2,
+                                 // largest |s_J|_2
 };
 constexpr size_t kScoresSmem = sizeof(ScoresSmem);
 
@@ -69,9 +74,9 @@ struct ScoresArgs {
   SeqMap m;
   const void* q;
   const float* q_scale;
-  const u16* kmean16;   // kbar rounded to bf16 [Hkv, NK, 128]
-  const float* kres;    // residual bound of each pooled key [Hkv, NK]
-  const float* bnorm;   // |bf16(kbar_J)|_2 of each pooled key [Hkv, NK] (rounded up)
+  const u16* kmean16;   // s_J = bf16(softmax_scale log2(e) kbar_J) [Hkv, NK, 128]
+  const float* kres;    // residual bound of each pooled key [Hkv, NK] (log2 units)
+  const float* bnorm;   // |s_J|_2 of each pooled key [Hkv, NK] (rounded up)
   float* scores;
   float* errb;          // per score row: bound on the error of its entries
   int64_t num_blocks;   // NK (pooled rows per KV head)
@@ -80,7 +85,6 @@ struct ScoresArgs {
   int lists, kvdiv;                // list owners (score rows per query block); owner o
                                    // reads the pooled keys of KV head o / kvdiv
   int cparts;           // workgroups per (kv head, query block), each over a range of key tiles
-  float logit_scale;
 };
 
 // Q fragment of one 32-row chunk: lane l holds row l%32, head-dim elements
@@ -168,11 +172,13 @@ __device__ __forceinline__ float2 column_stats(const f32x16* acc, const float* c
   return make_float2(m, pair_sum(s));
 }
 
-// Slice KK (0..7) of the column exp-sum of one finished 32-key chunk against
-// the column's reference ref (an upper bound of every logit of the column,
-// see ref_column), spread over the eight head-dim steps of the next chunk's
-// MFMAs: four of the 32 (row chunk, row) elements per slice, in order.
-template <bool MASKED, int KK>
+// Slice KK (0..7) of the column exp-sum of one finished 32-key chunk, spread
+// over the eight head-dim steps of the next chunk's MFMAs: four of the 32
+// (row chunk, row) elements per slice, in order.  DIRECT: sum of 2^x (every
+// logit of the pass at most kDirectMax, csc = 1); otherwise sum of
+// 2^(x csc - ref) against the column's reference ref (an upper bound of every
+// logit of the column).
+template <bool MASKED, bool DIRECT, int KK>
 __device__ __forceinline__ void sum_slice(const f32x16* acc, const float* csc, const int* nval,
                                           int half, float ref, float& s) {
   if constexpr (KK == 0) s = 0.f;
@@ -180,10 +186,15 @@ __device__ __forceinline__ void sum_slice(const f32x16* acc, const float* csc, c
   for (int e = 4 * KK; e < 4 * KK + 4; ++e) {
     const int rc = e >> 4, i = e & 15;
     const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-    const float x = __builtin_amdgcn_exp2f(fmaf(acc[rc][i], csc[rc], -ref));
+    const float x = __builtin_amdgcn_exp2f(DIRECT ? acc[rc][i] : fmaf(acc[rc][i], csc[rc], -ref));
     s += (!MASKED || row < nval[rc]) ? x : 0.f;
   }
 }
+
+// Largest logit bound (log2 units) for which the exp-sums run without a
+// reference: a term is then at most 2^112 and a column of a pass sums at most
+// 512 of them, so no sum overflows.
+constexpr float kDirectMax = 112.f;
 
 // A column's exp-sum against its reference is trusted when it is at least
 // kSumFloor: its largest term is then >= 2^-75, a normal float, and terms
@@ -205,7 +216,7 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&qf)[kRC][8], int kk, bf1
 // two MFMAs issue one by one, each followed by a share of the statistics
 // (independent VALU work that the in-order wave issues while the matrix core
 // runs).  Scheduling fences between steps keep this order.
-template <bool MASKED>
+template <bool MASKED, bool DIRECT>
 __device__ __forceinline__ float2 chunk_overlapped(const u16* bh, int jc, int col,
                                                    int half, const bf16x8 (&qf)[kRC][8],
                                                    f32x16* acc, const f32x16* prev,
@@ -221,14 +232,14 @@ __device__ __forceinline__ float2 chunk_overlapped(const u16* bh, int jc, int co
     bf16x8 nh;                                               \
     if constexpr (KK < 7) nh = opnd(bh, KK + 1);             \
     mma_step(qf, KK, vh, acc);                               \
-    sum_slice<MASKED, KK>(prev, csc, nval, half, ref, s);    \
+    sum_slice<MASKED, DIRECT, KK>(prev, csc, nval, half, ref, s); \
     interleave<2, 1>();                                      \
     __builtin_amdgcn_sched_barrier(0);                       \
     if constexpr (KK < 7) vh = nh;                           \
   }
   FP_STEP(0) FP_STEP(1) FP_STEP(2) FP_STEP(3) FP_STEP(4) FP_STEP(5) FP_STEP(6) FP_STEP(7)
 #undef FP_STEP
-  return make_float2(ref, pair_sum(s));
+  return make_float2(DIRECT ? 0.f : ref, pair_sum(s));
 }
 
 // Statistics of a finished chunk against the column reference, falling back
@@ -246,27 +257,28 @@ __device__ __forceinline__ float2 checked(float2 st, const f32x16* acc, const fl
   return st;
 }
 
-// Sum against the reference without interleaving (chunks outside the
-// pipeline), with the same fallback.
-template <bool MASKED>
+// The same sums without interleaving (chunks outside the pipeline), with the
+// same fallback.
+template <bool MASKED, bool DIRECT>
 __device__ __forceinline__ float2 ref_stats(const f32x16* acc, const float* csc, const int* nval,
                                             int half, float ref) {
   float s;
-  sum_slice<MASKED, 0>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 1>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 2>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 3>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 4>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 5>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 6>(acc, csc, nval, half, ref, s);
-  sum_slice<MASKED, 7>(acc, csc, nval, half, ref, s);
-  return checked<MASKED>(make_float2(ref, pair_sum(s)), acc, csc, nval, half);
+  sum_slice<MASKED, DIRECT, 0>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 1>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 2>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 3>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 4>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 5>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 6>(acc, csc, nval, half, ref, s);
+  sum_slice<MASKED, DIRECT, 7>(acc, csc, nval, half, ref, s);
+  return checked<MASKED>(make_float2(DIRECT ? 0.f : ref, pair_sum(s)), acc, csc, nval, half);
 }
 
 // One LDS tile for this wave.  Full tiles (kJC chunks) run as one basic block
 // with two accumulator sets: chunk j+1's MFMAs overlap chunk j's statistics.
-// ref[jc]: the reference of this lane's key column in chunk jc.
-template <bool MASKED>
+// ref[jc]: the reference of this lane's key column in chunk jc (unused when
+// DIRECT).
+template <bool MASKED, bool DIRECT>
 __device__ __forceinline__ void tile_chunks(const u16* bh, int njc, int col,
                                             int half, const bf16x8 (&qf)[kRC][8],
                                             const float* csc, const int* nval, const float* ref,
@@ -277,13 +289,16 @@ __device__ __forceinline__ void tile_chunks(const u16* bh, int njc, int col,
     mma_chunk(bh, 0, col, half, qf, acc0);
     __builtin_amdgcn_sched_barrier(0);
     // each chunk's sums are checked before its accumulators are reused
-    const float2 s0 = checked<MASKED>(chunk_overlapped<MASKED>(bh, 1, col, half, qf, acc1, acc0, csc, nval, ref[0]),
-                                      acc0, csc, nval, half);
-    const float2 s1 = checked<MASKED>(chunk_overlapped<MASKED>(bh, 2, col, half, qf, acc0, acc1, csc, nval, ref[1]),
-                                      acc1, csc, nval, half);
-    const float2 s2 = checked<MASKED>(chunk_overlapped<MASKED>(bh, 3, col, half, qf, acc1, acc0, csc, nval, ref[2]),
-                                      acc0, csc, nval, half);
-    const float2 s3 = ref_stats<MASKED>(acc1, csc, nval, half, ref[3]);
+    const float2 s0 = checked<MASKED>(
+        chunk_overlapped<MASKED, DIRECT>(bh, 1, col, half, qf, acc1, acc0, csc, nval, ref[0]),
+        acc0, csc, nval, half);
+    const float2 s1 = checked<MASKED>(
+        chunk_overlapped<MASKED, DIRECT>(bh, 2, col, half, qf, acc0, acc1, csc, nval, ref[1]),
+        acc1, csc, nval, half);
+    const float2 s2 = checked<MASKED>(
+        chunk_overlapped<MASKED, DIRECT>(bh, 3, col, half, qf, acc1, acc0, csc, nval, ref[2]),
+        acc0, csc, nval, half);
+    const float2 s3 = ref_stats<MASKED, DIRECT>(acc1, csc, nval, half, ref[3]);
     if (half == 0) {
       part[col] = s0;
       part[32 + col] = s1;
@@ -374,18 +389,25 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       const int64_t row_elem = ((tok0 + t0 + col) * a.hq + hq_idx) * (int64_t)kHeadDim;
       load_q_frag<QDT>(a.q, row_elem, rvalid, half, qf[rc]);
       qsf[rc] = QDT == FP_E4M3 ? a.q_scale[hq_idx] : 1.f;
-      csc[rc] = a.logit_scale * kLog2e * qsf[rc];
+      csc[rc] = qsf[rc];  // the keys carry softmax_scale log2(e)
     }
     // the first key tile does not depend on Q: in flight together with it
     stage(tile0, tile0 & 1);
     if (pass == 0) {
-      // largest residual bound of the row's key blocks (published by the
-      // barrier below), its loads in flight with the Q loads
+      // largest residual bound and largest |s_J| of the row's key blocks
+      // (published by the barrier below), loads in flight with the Q loads
       const float* kres = a.kres + (int64_t)(h / a.kvdiv) * a.num_blocks + qb.kb0;
-      float dm = 0.f;
-      for (int J = (int)threadIdx.x; J < ncols; J += 64 * kWaves) dm = fmaxf(dm, kres[J]);
+      float dm = 0.f, bm = 0.f;
+      for (int J = (int)threadIdx.x; J < ncols; J += 64 * kWaves) {
+        dm = fmaxf(dm, kres[J]);
+        if constexpr (QDT != FP_E4M3) bm = fmaxf(bm, bnbase[J]);  // e4m3: never direct
+      }
       dm = wave_max(dm);
-      if (lane == 0) sm.red[0][wave] = dm;
+      bm = wave_max(bm);
+      if (lane == 0) {
+        sm.red[0][wave] = dm;
+        sm.red[2][wave] = bm;
+      }
     }
     {
       // squared norms of this wave's rows (lanes l and l^32 hold the halves)
@@ -409,14 +431,20 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
 
     wait_vm();
     __syncthreads();
-    float qp2 = 0.f;  // largest squared query-row norm of this pass
+    float qp2 = 0.f, bmax = 0.f;  // largest squared query-row norm of this pass, largest |s_J|
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) qp2 = fmaxf(qp2, sm.red[1][w]);
+    for (int w = 0; w < kWaves; ++w) {
+      qp2 = fmaxf(qp2, sm.red[1][w]);
+      bmax = fmaxf(bmax, sm.red[2][w]);
+    }
     qn2 = fmaxf(qn2, qp2);
-    // reference of a key column: softmax_scale log2(e) max_r |q_r| |bf16(kbar_J)|
-    // bounds every logit x_rJ of the pass (Cauchy-Schwarz; the margin covers
-    // the fp32 accumulation and roundings), so exp2(x_rJ - ref) <= ~1
-    const float cref = a.logit_scale * kLog2e * __fsqrt_rn(qp2) * (1.f + 0x1p-10f);
+    // reference of a key column: max_r |q_r| |s_J| bounds every logit x_rJ of
+    // the pass (Cauchy-Schwarz; the margin covers the fp32 accumulation and
+    // roundings), so exp2(x_rJ - ref) <= ~1.  Below kDirectMax for every
+    // column of the row, the sums need no reference (bf16 / fp32 queries,
+    // whose logits carry no per-head scale).
+    const float cref = __fsqrt_rn(qp2) * (1.f + 0x1p-10f);
+    const bool direct = QDT != FP_E4M3 && cref * bmax <= kDirectMax;
 
     for (int tile = tile0; tile < tile1; ++tile) {
       const int buf = tile & 1;
@@ -424,12 +452,21 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
       const int njc = min(kJC, (ncols - tile * kJT + 31) >> 5);
       const u16* bh = sm.kb[buf];
       float ref[kJC];
+      if (direct) {
 #pragma unroll
-      for (int jc = 0; jc < kJC; ++jc) ref[jc] = cref * sm.bn[buf][jc * 32 + col];
-      if (masked)
-        tile_chunks<true>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
-      else
-        tile_chunks<false>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
+        for (int jc = 0; jc < kJC; ++jc) ref[jc] = 0.f;
+        if (masked)
+          tile_chunks<true, true>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
+        else
+          tile_chunks<false, true>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
+      } else {
+#pragma unroll
+        for (int jc = 0; jc < kJC; ++jc) ref[jc] = cref * sm.bn[buf][jc * 32 + col];
+        if (masked)
+          tile_chunks<true, false>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
+        else
+          tile_chunks<false, false>(bh, njc, col, half, qf, csc, nval, ref, sm.part[buf][wave]);
+      }
 
       wait_vm();
       __syncthreads();
@@ -461,14 +498,14 @@ __global__ __launch_bounds__(512) void scores_kernel(ScoresArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    // every entry of the row: |L_fast - L| <= softmax_scale * max_r |q_r| *
-    // max_J kres_J (+ the fp32 rounding of the statistics); the factor covers
-    // the rounding of the bound itself.  Workgroups sharing a row (cparts > 1)
-    // store the same value.
+    // every entry of the row: |L_fast - L| <= ln 2 * max_r |q_r| * max_J
+    // kres_J (+ the fp32 rounding of the statistics; kres is in log2 units,
+    // L in natural log); the factor covers the rounding of the bound itself.
+    // Workgroups sharing a row (cparts > 1) store the same value.
     float dm = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) dm = fmaxf(dm, sm.red[0][w]);
-    a.errb[(int64_t)h * a.num_qblocks + gq] = a.logit_scale * __fsqrt_rn(qn2) * dm * (1.f + 0x1p-10f);
+    a.errb[(int64_t)h * a.num_qblocks + gq] = kLn2 * __fsqrt_rn(qn2) * dm * (1.f + 0x1p-10f);
   }
 }
 
@@ -510,7 +547,6 @@ hipError_t launch_scores(const Geometry& g, const SeqMap& m, const void* q, cons
   a.lists = g.lists;
   a.kvdiv = g.kvdiv;
   a.max_blocks = g.max_blocks;
-  a.logit_scale = g.softmax_scale;
   if (g.qk_dtype == FP_BF16) return launch_scores_t<FP_BF16>(a, grid, st);
   if (g.qk_dtype == FP_E4M3) return launch_scores_t<FP_E4M3>(a, grid, st);
   if (g.qk_dtype == FP_F32) return launch_scores_t<FP_F32>(a, grid, st);

@@ -177,18 +177,20 @@ const char* fp_last_error(void);
  * block is a subtraction of max_J of this value (done by fp_select).
  * Entries with J > I are left unspecified.
  *
- * The dot products run on bf16 MFMA with kbar rounded (once) to bf16 and
- * fp32 accumulation.  After the Lo * NQ * n_max scores, block_scores holds
- * one float per score row (same row order): a bound E on how far the dot
- * products can move any entry of the row from exact arithmetic,
- *     E = softmax_scale * max_r |q_r|_2 *
- *         max_{J<=I} (|kbar_J - bf16(kbar_J)|_2 + 2^-15 |bf16(kbar_J)|_2)
- * (Cauchy-Schwarz on the rounding of the exact mean kbar_J, plus twice the
- * worst case of an fp32 sum of 128 exact products with any faithful
- * rounding; |q_r| includes q_scale for e4m3; a log-sum-exp over rows moves
- * by at most its largest shift), which fp_select uses.  The fp32 statistics
- * (exp2 / log2 / sums) add an absolute error below 1e-4 and a relative one
- * below 2^-19 of |L| on top of E.
+ * The dot products run on bf16 MFMA against s_J = bf16(c kbar_J), the exact
+ * mean scaled by c = softmax_scale * log2(e) in float64 and rounded once,
+ * with fp32 accumulation (log2-domain logits).  After the Lo * NQ * n_max
+ * scores, block_scores holds one float per score row (same row order): a
+ * bound E on how far the dot products can move any entry of the row from
+ * exact arithmetic,
+ *     E = ln(2) * max_r |q_r|_2 *
+ *         max_{J<=I} (|c kbar_J - s_J|_2 + 2^-15 |s_J|_2)
+ * (Cauchy-Schwarz on the rounding of c kbar_J, plus twice the worst case of
+ * an fp32 sum of 128 exact products with any faithful rounding; |q_r|
+ * includes q_scale for e4m3; a log-sum-exp over rows moves by at most its
+ * largest shift), which fp_select uses.  The fp32 statistics (exp2 / log2 /
+ * sums) add an absolute error below 1e-4 and a relative one below 2^-19 of
+ * |L| on top of E.
  *
  * q, k_cache, v_cache: inputs (layouts above).  k_mean, v_mean, block_scores:
  * outputs.  ws: FP_WS_DISCOVER workspace.

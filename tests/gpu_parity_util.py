@@ -18,16 +18,19 @@ TOL_OUT = {"bf16": 2e-2, "f32": 2e-2, "e4m3": 6e-2}
 # (|q|, |kbar| ~ 17) that is a few 1e-2 in the worst case, and the lse moves
 # by at most the largest such shift.
 TOL_LSE = 5e-2
-# pooled block scores (natural-log units): the fast path rounds kbar to bf16
-# and accumulates the exact bf16 products in fp32.  Per score row the error
-# is bounded by score_bound() below (rounding + accumulation); the fp32
-# statistics (exp2, sums, log) add less than TOL_SCORE_STATS.
+# pooled block scores (natural-log units): the fast path rounds
+# softmax_scale log2(e) kbar to bf16 and accumulates the exact bf16 products
+# in fp32 (log2-domain logits).  Per score row the error is bounded by
+# score_bound() below (rounding + accumulation); the fp32 statistics (exp2,
+# sums, log) add less than TOL_SCORE_STATS.
 TOL_SCORE_STATS = 1e-3
 # pooled means: float64 sums of the stored values and one division, on both
 # sides (relative to max(1, |mean|))
 TOL_POOL = 1e-12
 # fp32 accumulation allowance of a 128-term dot product of exact products
 ACCUM_REL = 2.0 ** -15
+LOG2E = 1.4426950408889634
+LN2 = 0.6931471805599453
 
 
 def bf16_round64(x):
@@ -45,21 +48,22 @@ def bf16_round64(x):
 
 def score_bound(prob, k_mean, h, s, I):
     """Bound on |fast - exact| block score of row (h, s, I), derived from the
-    fast path's arithmetic: rounding the exact mean kbar_J to bf16 moves x_rJ
-    by at most scale |q_r| |kbar_J - bf16(kbar_J)| (Cauchy-Schwarz), and fp32
-    accumulation of 128 exact products by at most scale |q_r| ACCUM_REL
-    |bf16(kbar_J)|; a log-sum-exp over rows moves by at most the largest
-    shift.  k_mean: float64 pooled keys (the library's, checked against the
-    oracle's separately, or the oracle's own)."""
+    fast path's arithmetic: with c = scale log2(e) and s_J = bf16(c kbar_J),
+    the log2-domain logit q_r . s_J is off c q_r . kbar_J by at most
+    |q_r| |c kbar_J - s_J| (Cauchy-Schwarz) plus |q_r| ACCUM_REL |s_J| (fp32
+    accumulation of 128 exact products); a log-sum-exp over rows moves by at
+    most the largest shift, ln 2 of it in natural-log units.  k_mean: float64
+    pooled keys (the library's, checked against the oracle's separately, or
+    the oracle's own)."""
     B = prob.block_size
     nI = min(B, prob.seqlen(s) - I * B)
     qg = prob.queries(s, prob.list_heads(h), I * B + np.arange(nI)).reshape(-1, prob.d)
     qn = float(np.sqrt((qg * qg).sum(1)).max())
     kb0 = int(prob.block_offsets()[s])
-    km = k_mean[prob.list_kv_head(h), kb0:kb0 + I + 1].astype(np.float64)
+    km = k_mean[prob.list_kv_head(h), kb0:kb0 + I + 1].astype(np.float64) * (prob.scale * LOG2E)
     hi = bf16_round64(km)
     res = np.sqrt(((km - hi) ** 2).sum(1)) + ACCUM_REL * np.sqrt((hi * hi).sum(1))
-    return prob.scale * qn * float(res.max())
+    return LN2 * qn * float(res.max())
 
 
 def log(msg):
