@@ -16,16 +16,16 @@ from gpu_parity_util import compare, log, run_gpu, score_bound
 pytestmark = pytest.mark.gpu
 
 
-def wide_band_workload(c):
-    """Every query of KV group h gets c * u_h added, u_h a unit vector
-    orthogonal to all pooled keys of KV head h (fewer blocks than dimensions):
-    the pooled logits barely move, the query norms, and with them the fast
-    scores' error bound, grow with c."""
+def wide_band_workload(c, groups=None):
+    """Every query of KV group h (of `groups`, default all) gets c * u_h
+    added, u_h a unit vector orthogonal to all pooled keys of KV head h (fewer
+    blocks than dimensions): the pooled logits barely move, the query norms,
+    and with them the fast scores' error bound, grow with c."""
     w = make_workload(custom_spec((3000, 1100), 8, 2, page_size=32, seed=4242, name="wideband"))
     prob = OracleProblem.from_workload(w)
     q = decode_bf16(w.q).astype(np.float64)
     g = prob.group
-    for h in range(prob.hkv):
+    for h in (range(prob.hkv) if groups is None else groups):
         kb = np.concatenate([pool_blocks(prob.keys(s, h), prob.block_size)[0]
                              for s in range(prob.num_seqs)])
         u = np.linalg.svd(kb)[2][-1]  # right singular vector of a zero singular value
@@ -61,3 +61,24 @@ def test_wide_error_band_parity(alpha):
     g = run_gpu(w, alpha)
     stats = compare(w, g, alpha)
     assert stats["score_bound"] > 0.2
+
+
+def test_mixed_score_paths_parity():
+    """One launch where the discovery sums take both forms: KV group 0's
+    queries are pushed to logit bounds far above 112 log2 units (sums against
+    a per-column reference), group 1 keeps its ~60 (reference-free sums).
+    Both groups' scores, lists and outputs match the oracle."""
+    w = wide_band_workload(200.0, groups=[0])
+    prob = OracleProblem.from_workload(w)
+    c = prob.scale * 1.4426950408889634
+    for h, want_direct in ((0, False), (1, True)):
+        kb = np.concatenate([pool_blocks(prob.keys(s, h), prob.block_size)[0]
+                             for s in range(prob.num_seqs)])
+        qs = np.concatenate([prob.queries(s, prob.list_heads(h), np.arange(prob.seqlen(s))).reshape(-1, prob.d)
+                             for s in range(prob.num_seqs)])
+        bound = c * np.sqrt((qs * qs).sum(1)).max() * np.sqrt((kb * kb).sum(1)).max()
+        log(f"  group {h}: logit bound {bound:.1f} log2 units")
+        assert (bound < 100.0) == want_direct
+    g = run_gpu(w, 0.1)
+    stats = compare(w, g, 0.1)
+    log(f"  mixed paths: {stats}")
