@@ -13,7 +13,7 @@
 //     of one query block, split over 8 waves (two per SIMD, one 32-row chunk
 //     each).  The g/2 workgroups of a group get ids 8 apart, i.e. the same
 //     XCD at about the same time, so their K/V reads share that L2; the last
-//     15 % of the items are handed out on demand so that the XCDs finish
+//     7 % of the items are handed out on demand so that the XCDs finish
 //     together.
 //   * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no staging
 //     registers): every lane gathers 16 bytes of a token row through the page
@@ -68,7 +68,7 @@ constexpr int kAttnWaves = 8;
 // On-demand tail of the item order (launches of at least kAttnDynMinItems
 // items): its share of the items and the extra workgroups, in percent of it.
 constexpr int64_t kAttnDynMinItems = 4096;
-constexpr int64_t kAttnDynFracPct = 15;
+constexpr int64_t kAttnDynFracPct = 7;
 constexpr int64_t kAttnDynSlackPct = 50;
 
 struct AttnArgs {
