@@ -52,3 +52,26 @@ def test_full_lists_count_every_causal_pair():
     assert kp == bench.causal_pairs(spec.seqlens) * spec.num_q_heads
     rp, _ = _csr(_group_csr(spec, None, full=True))
     assert rp[-1] == bench.causal_blocks(spec.seqlens, spec.num_kv_heads)
+
+
+def test_cpu_baseline_times_each_oracle_stage():
+    """The oracle leg on a small prompt: every query block of the sample is
+    run once through scores, selection and attention, each stage timed, and
+    the rate counts the same kept pairs as the oracle's own selection."""
+    from oracle import OracleProblem, run_pipeline
+    from synthetic import make_workload, spec_for
+    w = make_workload(spec_for("toy_2k"))
+    r = bench.cpu_baseline(w, 0.1, True, budget_s=60.0)
+    st = r["stages_s"]
+    assert st["rows"] == 16 and r["kind"] == "oracle" and r["cores"] >= 1
+    assert all(st[k] > 0 for k in ("decode_pool_sequence", "score", "select", "attend"))
+    # the pairs behind the rate: the oracle pipeline's own lists
+    prob = OracleProblem.from_workload(w)
+    res = run_pipeline(prob, 0.1, attend=False)
+    B, d, g = w.spec.block_size, w.spec.head_dim, w.spec.group
+    flops = 0
+    for (h, s, I), x in res.items():
+        nI = min(B, w.spec.seqlens[s] - I * B)
+        flops += 4 * d * g * (int(np.sum(np.asarray(x["kept"]) < I)) * B * nI + nI * (nI + 1) // 2)
+    secs = st["score"] + st["select"] + st["attend"]
+    assert 0.5 < flops / 1e12 / r["value"] / secs < 1.5
