@@ -71,11 +71,12 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0, head_lists=False):
+def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0, head_lists=False,
+            softmax_scale=0.0):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
     db = upload(w, "cuda")
-    pipe = Pipeline(db, attn_splits=attn_splits, head_lists=head_lists)
+    pipe = Pipeline(db, softmax_scale=softmax_scale, attn_splits=attn_splits, head_lists=head_lists)
     pipe.run(alpha, sinks, local, correction)
     torch.cuda.synchronize()
     rp, ci = pipe.csr()
@@ -94,12 +95,16 @@ def run_gpu(w, alpha, sinks=256, local=512, correction=True, attn_splits=0, head
 
 
 def compare(w, g, alpha, sinks=256, local=512, correction=True, rows=None,
-            check_pool=True, head_lists=False):
+            check_pool=True, head_lists=False, softmax_scale=0.0):
     """Compare GPU results `g` with the oracle on `rows` ((owner, s, I)
     triples; default all; the owner is the KV head, or the query head with
-    head_lists).  Returns a stats dict; raises AssertionError on failure."""
+    head_lists).  softmax_scale: the one the library was given (0: 1/sqrt(d);
+    the oracle takes the library's float32 value).  Returns a stats dict;
+    raises AssertionError on failure."""
     prob = OracleProblem.from_workload(w)
     prob.head_lists = head_lists
+    if softmax_scale > 0:
+        prob.softmax_scale = float(np.float32(softmax_scale))
     spec = w.spec
     qoff = prob.query_block_offsets()
     t0 = time.time()

@@ -59,6 +59,25 @@ def test_small_full_parity(name, kw, alpha, sinks, local, corr, splits):
     compare(w, g, alpha, sinks, local, corr)
 
 
+@pytest.mark.parametrize("qk", ["bf16", "e4m3"])
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_softmax_scale_parity(scale, qk):
+    """A softmax scale other than 1/sqrt(d): the discovery keys (pre-scaled
+    by it), the exact re-check and the attention logits all follow it.  At
+    0.3 the bf16 discovery's per-row logit bounds run from ~100 to ~190 log2
+    units, on both sides of the 112 up to which the sums need no reference
+    (both forms of the sums run); at 0.05 they stay below ~32."""
+    log(f"case softmax_scale={scale} {qk}")
+    kw = dict(seqlens=(1500, 640), num_q_heads=16, num_kv_heads=2, page_size=64,
+              paging="roundrobin", seed=130)
+    if qk == "e4m3":
+        kw.update(qk_dtype="e4m3", v_dtype="bf16")
+    w = make_workload(custom_spec(name=f"scale_{qk}_{scale}", **kw))
+    g = run_gpu(w, 0.1, softmax_scale=scale)
+    stats = compare(w, g, 0.1, softmax_scale=scale)
+    log(f"  {stats}")
+
+
 def test_toy_2k_config_full_parity():
     """2048-token single prompt, fp32 inputs, contiguous KV, g = 4."""
     log("case toy_2k")
