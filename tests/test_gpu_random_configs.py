@@ -1,8 +1,9 @@
 """Seeded random small configurations on the GPU, each compared in full with
 the oracle: GQA factor, head counts, page size and paging, ragged lengths
 (incl. one-token sequences and partial blocks), cached prefixes, dtypes,
-output dtype, alpha, sinks / window, correction, per-query-head lists and
-the KV split, drawn together so that their combinations are exercised.
+output dtype, alpha, sinks / window, correction, per-query-head lists, the
+KV split and the softmax scale, drawn together so that their combinations
+are exercised.
 The draws are fixed by the seed; the printed line names the case."""
 
 import numpy as np
@@ -14,7 +15,7 @@ from gpu_parity_util import compare, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 16
+N_CASES = 24
 
 
 def draw(seed):
@@ -40,6 +41,9 @@ def draw(seed):
                 sinks=int(rng.choice([0, 128, 256])), local=int(rng.choice([128, 512])),
                 correction=bool(rng.random() < 0.75), head_lists=bool(rng.random() < 0.3),
                 splits=int(rng.choice([0, 1, 3])))
+    # drawn last, so the draws above stay those of the earlier cases; 0 is
+    # the default 1/sqrt(d)
+    opts["scale"] = float(rng.choice([0.0, 0.0, 0.04, 0.2]))
     return kw, ctx, opts
 
 
@@ -51,5 +55,6 @@ def test_random_config_full_parity(seed):
     if ctx is not None:
         w = chunk_view(w, ctx)
     g = run_gpu(w, o["alpha"], o["sinks"], o["local"], o["correction"], attn_splits=o["splits"],
-                head_lists=o["head_lists"])
-    compare(w, g, o["alpha"], o["sinks"], o["local"], o["correction"], head_lists=o["head_lists"])
+                head_lists=o["head_lists"], softmax_scale=o["scale"])
+    compare(w, g, o["alpha"], o["sinks"], o["local"], o["correction"], head_lists=o["head_lists"],
+            softmax_scale=o["scale"])
