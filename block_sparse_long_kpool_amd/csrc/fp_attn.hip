@@ -206,7 +206,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   const int hh = 2 * pack + (wave * RC) / 4;
   const bool head_ok = hh < a.group;
   const int hq_idx = __builtin_amdgcn_readfirstlane(h * a.group + (head_ok ? hh : 0));  // wave-uniform
-  const int tbase = 32 * ((wave * RC) % 4);
+  // 32-token slice of the wave.  Waves w and w + 4 share a SIMD; in the
+  // sparse instance they take complementary slices (s and 3 - s) so that
+  // every SIMD has the same causal work in the diagonal tile, whose chunks
+  // past a wave's last row are skipped (the dense instance, where the
+  // diagonal tile is one of many, keeps slice w % 4).
+  const int slice = DENSE ? wave % 4 : (wave < 4 ? wave : 7 - wave);
+  const int tbase = 32 * slice;
 
   // ---- Q^T fragments (B operand), kept for the whole kernel ----
   // (issued right after the list: their latency overlaps the list set-up
