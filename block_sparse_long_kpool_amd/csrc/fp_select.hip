@@ -159,7 +159,10 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   constexpr int kW = kMaxBlocksPerSeq / 32;
   __shared__ uint32_t keep_fast[kW + 1], cand_thr[kW + 1], cand_max[kW + 1], keep_fix[kW + 1];
   __shared__ float redf[kSelThreads / 64];
-  __shared__ int redi[kSelThreads / 64];
+  __shared__ int redi[kSelThreads / 64];  // the waves' candidate flags
+  // the waves' counts: a separate array, since without candidates no barrier
+  // separates a wave's count from another wave still reading the flags
+  __shared__ int redc[kSelThreads / 64];
   __shared__ double redd[kSelThreads / 64][kBatch];
   __shared__ __attribute__((aligned(16))) double kbs[kBatch * kHeadDim];
   __shared__ int bj[kBatch];
@@ -291,12 +294,12 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
     cnt += __popc(v);
   }
   cnt = (int)wave_sum((float)cnt);
-  if (lane == 0) redi[wave] = cnt;
+  if (lane == 0) redc[wave] = cnt;
   __syncthreads();
   if (tid == 0) {
     int tot = 0;
 #pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w) tot += redi[w];
+    for (int w = 0; w < kSelThreads / 64; ++w) tot += redc[w];
     counts[row] = tot;
   }
 }
@@ -474,6 +477,8 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void compact_kernel(int64_t nrows,
   const int words = (max_blocks + 31) >> 5;
   const uint32_t* bits = keep_bits + row * words;
   int32_t* dst = col_idx + row_ptr[row];
+  // the row's slot: never written past, whatever the bit row holds
+  const int cap = row_ptr[row + 1] - row_ptr[row];
   int base_out = 0;
   for (int base = 0; base < 32 * words; base += 64) {
     const int w = base >> 5;
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void compact_kernel(int64_t nrows,
     const unsigned long long m = ((unsigned long long)hi << 32) | lo;
     const bool keep = (m >> lane) & 1ull;
     const int pos = __popcll(m & ((1ull << lane) - 1ull));
-    if (keep) dst[base_out + pos] = base + lane;
+    if (keep && base_out + pos < cap) dst[base_out + pos] = base + lane;
     base_out += __popcll(m);
   }
 }
