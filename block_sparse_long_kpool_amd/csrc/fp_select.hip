@@ -169,9 +169,14 @@ __global__ __launch_bounds__(kSelThreads) void decide_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const int h = (int)(row / num_qblocks);
-  const QBlock qb = query_block(m, (int)(row % num_qblocks));
+  // heaviest rows first: last query block first, the list owners interleaved
+  // (a row's re-check work grows with its length; the long rows then do not
+  // form the launch's tail)
+  const int64_t lists = (int64_t)gridDim.x / num_qblocks;
+  const int h = (int)((int64_t)blockIdx.x % lists);
+  const int gq = (int)(num_qblocks - 1 - (int64_t)blockIdx.x / lists);
+  const int64_t row = (int64_t)h * num_qblocks + gq;
+  const QBlock qb = query_block(m, gq);
   const int I = qb.I;
   const int words = (max_blocks + 31) >> 5;
   uint32_t* bits = keep_bits + row * words;
