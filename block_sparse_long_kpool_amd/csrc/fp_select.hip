@@ -337,8 +337,11 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(
   extern __shared__ __attribute__((aligned(16))) char rank_smem[];
   RankSmem& sm = *reinterpret_cast<RankSmem*>(rank_smem);
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const QBlock qb = query_block(m, (int)(row % num_qblocks));
+  // heaviest rows (longest sorts) first, as in the threshold selection
+  const int64_t lists = (int64_t)gridDim.x / num_qblocks;
+  const int gq = (int)(num_qblocks - 1 - (int64_t)blockIdx.x / lists);
+  const int64_t row = ((int64_t)blockIdx.x % lists) * num_qblocks + gq;
+  const QBlock qb = query_block(m, gq);
   const int I = qb.I;
   const int ncols = I + 1;
   int P = 1;
