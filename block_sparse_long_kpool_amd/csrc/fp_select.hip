@@ -5,16 +5,17 @@
 // so the attention loop walks only them).
 //
 // Three kernels:
-//   decide  one workgroup (4 waves) per CSR row: re-weight (subtract the row
-//           max of the log scores), threshold, forced blocks -> keep bitmask
-//           + count.  Entries whose fast (bf16) score lies within the row's
-//           guard of the threshold are re-evaluated in float64 from q and
-//           k_mean by the whole workgroup, with the row maximum re-evaluated
-//           the same way, so that every decision matches exact arithmetic.
+//   decide  one workgroup (4 waves) per CSR row, heaviest rows first:
+//           re-weight (subtract the row max of the log scores), threshold,
+//           forced blocks -> keep bitmask + count.  Entries whose fast
+//           (bf16) score lies within the row's guard of the threshold are
+//           re-evaluated in float64 from q and k_mean by the whole
+//           workgroup, with the row maximum re-evaluated the same way, so
+//           that every decision matches exact arithmetic.
 //   scan    one workgroup: exclusive prefix sum of the counts -> row_ptr.
 //   compact one wave per row (kRowsPerWg rows per workgroup): wavefront
 //           ballot + popcount prefix writes the kept block indices in
-//           ascending order.
+//           ascending order, never past the row's slot of row_ptr.
 #include "fp_internal.hpp"
 
 namespace fp {
