@@ -30,7 +30,9 @@
 //     registers; A = V^T is read from the natural [key][d] LDS tile with
 //     ds_read_b64_tr_b16 (16x4 transposes inside 16-lane groups).
 //   * correction tiles: 128 pooled keys/values (bf16) per tile with a
-//     log2(n_J) bias; listed blocks and J > I are masked to -inf.
+//     log2(n_J) bias, which seeds the S^T accumulator (stored divided by
+//     the head's logit scale, so the softmax is that of a kept tile);
+//     listed blocks and J > I are masked to -inf the same way.
 //   * rows: query blocks of the call (a chunk's blocks after a cached prefix,
 //     or whole prompts); keys are every cached position up to the row.
 //   * KV split (small launches): a row's tile list is cut into contiguous
@@ -104,7 +106,7 @@ struct AttnArgs {
 struct SharedMem {
   u16 k[2][kTileElems];  // fp8 tiles use the first half of a buffer
   u16 v[2][kTileElems];
-  float bias[2][kBlock];
+  float bias[2][2][kBlock];  // [buffer][head slot]: log2(n_J) / c_pool or -inf
   // element offset ((page * page_size + offset) * Hkv + h) * d of each token
   // row of a kept tile in the paged K/V caches
   int64_t slot[2][kBlock];
@@ -279,6 +281,24 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   int tbeg = 0;
   int tend = nkept;
 
+  // log2-domain logit scales: kept tiles and pooled tiles
+  float c_kept = a.softmax_scale * kLog2e;
+  float c_pool = c_kept;
+  if constexpr (kFp8) {
+    const float qs = a.q_scale[hq_idx];
+    c_kept *= qs * a.k_scale[kvh];
+    c_pool *= qs;
+  }
+  // pooled-tile bias writers: thread t < 256 writes slot t / 128, whose head
+  // may differ from its own wave's; the bias is stored divided by that
+  // head's c_pool so that it can seed the MFMA accumulator
+  float c_pool_w = a.softmax_scale * kLog2e;
+  if constexpr (kFp8) {
+    const int hh_w = 2 * pack + (tid >> 7);
+    c_pool_w *= a.q_scale[h * a.group + (hh_w < a.group ? hh_w : 0)];
+  }
+  const int bslot = (wave * RC) / 4;  // this wave's head slot
+
   // ---- tile staging -------------------------------------------------------
   // Kept block J: token rows J*128 .. +127 of the sequence (rows past the end
   // of the sequence re-read the block's first token: finite values that the
@@ -321,11 +341,12 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   auto issue_tile = [&](int t, int buf) {
     const bool pooled = t >= nkept;
     const int idx = tile_index(t);
-    if (pooled && tid < kBlock) {
-      const int J = idx * kBlock + tid;
+    if (pooled && tid < 2 * kBlock) {
+      const int j = tid & (kBlock - 1);
+      const int J = idx * kBlock + j;
       const bool kept = (sm.kept_bits[J >> 5] >> (J & 31)) & 1u;
       const int nJ = min(kBlock, len - J * kBlock);
-      sm.bias[buf][tid] = (J <= I && !kept) ? __log2f((float)nJ) : -INFINITY;
+      sm.bias[buf][tid >> 7][j] = (J <= I && !kept) ? __log2f((float)nJ) / c_pool_w : -INFINITY;
     }
     const int64_t* slots = sm.slot[buf];
     if constexpr (kF32) {
@@ -445,15 +466,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   tbeg = (int)(((int64_t)split * ntiles) / a.splits);
   tend = (int)(((int64_t)(split + 1) * ntiles) / a.splits);
 
-  // log2-domain logit scales: kept tiles and pooled tiles
-  float c_kept = a.softmax_scale * kLog2e;
-  float c_pool = c_kept;
-  if constexpr (kFp8) {
-    const float qs = a.q_scale[hq_idx];
-    c_kept *= qs * a.k_scale[kvh];
-    c_pool *= qs;
-  }
-
   // ---- online-softmax state ----
   f32x16 o[RC][4];
   float m_run[RC], l_run[RC];
@@ -523,7 +535,21 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     // 4 half + i%4 in slot i
     auto qk = [&](int c, f32x16* sc) {
 #pragma unroll
-      for (int rc = 0; rc < RC; ++rc) sc[rc] = f32x16{};
+      for (int rc = 0; rc < RC; ++rc) {
+        if constexpr (POOLED) {
+          // the accumulator starts at the pooled keys' bias (in logit units)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const float4 bv = *reinterpret_cast<const float4*>(&sm.bias[buf][bslot][32 * c + 8 * jq + 4 * half]);
+            sc[rc][4 * jq + 0] = bv.x;
+            sc[rc][4 * jq + 1] = bv.y;
+            sc[rc][4 * jq + 2] = bv.z;
+            sc[rc][4 * jq + 3] = bv.w;
+          }
+        } else {
+          sc[rc] = f32x16{};
+        }
+      }
       if constexpr (kQk8) {
         const uint8_t* kb = reinterpret_cast<const uint8_t*>(kt) + c * 32 * 128;
 #pragma unroll
@@ -575,16 +601,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     auto finish_logits = [&](int c, f32x16* sc) {
 #pragma unroll
       for (int rc = 0; rc < RC; ++rc) {
-        if constexpr (POOLED) {
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const float4 bv = *reinterpret_cast<const float4*>(&sm.bias[buf][32 * c + 8 * jq + 4 * half]);
-            sc[rc][4 * jq + 0] = fmaf(sc[rc][4 * jq + 0], c_pool, bv.x);
-            sc[rc][4 * jq + 1] = fmaf(sc[rc][4 * jq + 1], c_pool, bv.y);
-            sc[rc][4 * jq + 2] = fmaf(sc[rc][4 * jq + 2], c_pool, bv.z);
-            sc[rc][4 * jq + 3] = fmaf(sc[rc][4 * jq + 3], c_pool, bv.w);
-          }
-        }
         if constexpr (DIAG) {
           const int p_local = tbase + 32 * rc + col;
 #pragma unroll
@@ -602,9 +618,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
         float lsum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float arg;
-          if constexpr (POOLED) arg = sc[rc][i] - m;
-          else arg = fmaf(sc[rc][i], c_kept, -m);
+          const float arg = fmaf(sc[rc][i], POOLED ? c_pool : c_kept, -m);
           const float pe = __builtin_amdgcn_exp2f(arg);
           lsum += pe;
           pp[rc][i >> 3][i & 7] = f32_to_bf16(pe);
@@ -633,7 +647,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
           float mloc = sc[rc][0];
 #pragma unroll
           for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, sc[rc][i]);
-          if constexpr (!POOLED) mloc *= c_kept;
+          mloc *= POOLED ? c_pool : c_kept;
           mloc = pair_max(mloc);
           const float m_old = m_run[rc];
           const float m_use = (mloc > m_old + kLazy) ? mloc : m_old;
