@@ -474,6 +474,10 @@ def main():
             "peak": round(peak, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
+            # the same launches counted on kept pairs only (the correction's
+            # FLOPs left out), against the peak of the kept pairs' contractions
+            "kept_pairs_frac": round(4 * d * kp / (t["attn_ms"] * 1e-3) / 1e12
+                                     / attn_peak(spec, kp, 0, False), 4),
             "traffic": traffic_for(spec.name) if args.alpha == 0.1 and correction else None,
             "flop_per_launch": attn_flop,
             "peak_basis": "QK^T at the %s MFMA rate, P.V and correction at bf16"
