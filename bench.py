@@ -128,6 +128,41 @@ def kept_pairs(row_ptr, col_idx, spec, ctx=None, head_lists=False):
     return kept * g, corr * g
 
 
+def recheck_counts(scores, errb, seqlens, alpha, sinks=256, local=512, B=128, batch=8):
+    """The selection's float64 re-check work, recounted on the host from the
+    fast scores and their per-row bounds (scores [owners, NQ, n_max], errb
+    [owners, NQ]; whole prompts): a row is re-checked when a non-forced entry
+    lies within its guard of the threshold, and then every such entry plus
+    every candidate for the row maximum is evaluated, in passes of `batch`
+    keys over the row's queries.  The guard is the selection's rule
+    (2 E + stat(l) + stat(lmax), stat(x) = 1e-3 + 2^-17 |x|, natural log),
+    taken here in float64, so an entry right at a guard's edge may count
+    differently from the kernel's fp32 test."""
+    I = np.concatenate([np.arange(-(-n // B)) for n in seqlens])
+    J = np.arange(scores.shape[2])
+    valid = J[None, :] <= I[:, None]
+    n_sink = -(-sinks // B)
+    n_local = max(1, -(-local // B))
+    forced = (J[None, :] < n_sink) | (I[:, None] - J[None, :] < n_local)
+    rows = evals = passes = 0
+    for o in range(scores.shape[0]):
+        L = np.where(valid, scores[o].astype(np.float64), -np.inf)
+        lmax = L.max(axis=1)
+        thr = np.log(alpha) + lmax
+        g0 = 2.0 * errb[o].astype(np.float64) + 1e-3 + 2.0 ** -17 * np.abs(lmax)
+        with np.errstate(invalid="ignore"):
+            g = g0[:, None] + 1e-3 + 2.0 ** -17 * np.abs(np.where(valid, L, 0.0))
+            ct = valid & ~forced & (np.abs(L - thr[:, None]) <= g)
+            cm = valid & (L >= lmax[:, None] - g)
+        need = ct.any(axis=1)
+        ev = np.where(need, ct.sum(axis=1) + cm.sum(axis=1), 0)
+        rows += int(need.sum())
+        evals += int(ev.sum())
+        passes += int((-(-ev // batch)).sum())
+    return {"rows_rechecked": rows, "rows": int(scores.shape[0] * len(I)),
+            "evaluations": evals, "passes": passes}
+
+
 def gpu_setup(spec, threads=None, ctx=None, attn_splits=0, head_lists=False):
     import torch
     from block_sparse_long_kpool_amd import Pipeline, upload
@@ -485,6 +520,11 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if select is None and ctx is None and not hl and args.alpha > 0:
+        # the selection's float64 re-check work on the timed step's scores
+        line["selection"] = recheck_counts(pipe.scores.cpu().numpy(),
+                                           pipe.scores_err.cpu().numpy(), spec.seqlens,
+                                           args.alpha)
     # the oracle (cpu_baseline) leg: first the correctness of the timed step
     # (before any other configuration overwrites its results), at the end the
     # oracle's own throughput on a bounded sample

@@ -75,3 +75,37 @@ def test_cpu_baseline_times_each_oracle_stage():
         flops += 4 * d * g * (int(np.sum(np.asarray(x["kept"]) < I)) * B * nI + nI * (nI + 1) // 2)
     secs = st["score"] + st["select"] + st["attend"]
     assert 0.5 < flops / 1e12 / r["value"] / secs < 1.5
+
+
+def test_recheck_counts_follow_the_selection_guard():
+    """The bench's recount of the float64 re-check work: a row is re-checked
+    only when a non-forced entry lies within its guard of the threshold
+    (sink and window blocks and entries past the diagonal never count), and
+    then its threshold and maximum candidates are evaluated in passes of 8
+    keys.  Sinks: J < 2; window: I - J < 4."""
+    nq = 20
+    seqlens = (128 * nq,)
+    L = np.full((1, nq, nq), np.nan, np.float32)  # entries past the diagonal: garbage
+    for I in range(nq):
+        L[0, I, :I + 1] = -10.0
+        L[0, I, 0] = 0.0  # the row maximum, on a sink block
+    E = np.full((1, nq), 0.01, np.float32)
+    thr = np.log(0.1)
+    L[0, 9, 3] = thr + 0.002    # within 2E + stat of the threshold, not forced
+    L[0, 8, 7] = thr            # in the window: forced, not a candidate
+    L[0, 7, 1:7] = thr - 0.001  # J = 1 (sink) and 4..6 (window) forced; J = 2, 3 candidates
+    L[0, 6, 2] = thr + 0.5      # far outside the guard
+    L[0, 19, 1:20] = thr        # J = 2..15 candidates (14), the rest forced
+    got = bench.recheck_counts(L, E, seqlens, 0.1)
+    assert got["rows"] == nq
+    assert got["rows_rechecked"] == 3
+    # each re-checked row also evaluates its maximum (J = 0)
+    assert got["evaluations"] == (1 + 1) + (2 + 1) + (14 + 1)
+    assert got["passes"] == 1 + 1 + 2
+    # a second list owner with no entry near its threshold adds nothing
+    L2 = np.concatenate([L, np.where(np.isnan(L), np.nan, -10.0).astype(np.float32)])
+    L2[1, :, 0] = 0.0
+    got2 = bench.recheck_counts(L2, np.concatenate([E, E]), seqlens, 0.1)
+    assert got2["rows"] == 2 * nq
+    assert {k: got2[k] for k in ("rows_rechecked", "evaluations", "passes")} == \
+        {k: got[k] for k in ("rows_rechecked", "evaluations", "passes")}
