@@ -6,6 +6,8 @@ KV split and the softmax scale, drawn together so that their combinations
 are exercised.
 The draws are fixed by the seed; the printed line names the case."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -15,7 +17,8 @@ from gpu_parity_util import compare, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+# 200 by default (about 40 s); FP_RANDOM_CASES=N runs seeds 0 .. N-1
+N_CASES = int(os.environ.get("FP_RANDOM_CASES", "200"))
 
 
 def draw(seed):
